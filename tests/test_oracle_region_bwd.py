@@ -1,0 +1,23 @@
+"""Pins of the oracle's backward (see tests/oracle_pins.py)."""
+import pytest
+
+import oracle_pins as pins
+
+
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+def test_finite_differences(norm):
+    pins.check_backward_finite_differences(norm)
+
+
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+def test_torch_autograd(norm):
+    pins.check_backward_matches_torch_autograd(norm)
+
+
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+def test_scale_identities(norm):
+    pins.check_backward_scale_identities(norm)
+
+
+def test_dbeta_is_column_sum():
+    pins.check_dbeta_is_column_sum()
