@@ -1,0 +1,274 @@
+"""Benchmark of the fused SP-region forward + backward on one MI355X.
+
+One step = forward (g* slab sum, bias, dropout, residual, LayerNorm) and
+backward (dx, dgamma, dbeta) of the region on one rank's shard.  Default
+workload: the 70B-shaped shard of hpc.payai.win lesson 7's worked example
+(s = 16384, b = 1, h = 8192, t = 8 -> 2048 local tokens, bf16, p = 0.1).
+Inputs are synthetic (seeded) and resident in HBM before timing starts;
+several input/output sets rotate so that consecutive steps do not hit the
+256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--sets R]
+  python bench.py --summarize-rocprof DIR   # rocprofv3 output -> text summary
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+METRIC = "SP-region fwd+bwd tokens/s and achieved HBM GB/s (% of peak), h=8192 shard"
+FWD_KERNEL_SOURCES = ["layernorm_sp_region_amd/csrc/fwd.hip", "layernorm_sp_region_amd/csrc/spr_device.h"]
+TRAFFIC_FILE = "profiles/traffic_sp_region_fwd_kernel_shard70b.txt"
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic bytes: every input read once, every output written once.
+# ---------------------------------------------------------------------------
+def fwd_bytes(w, T):
+    E, h = w.elem_bytes, w.h
+    params = sum([w.has_bias, True, w.has_beta]) * h * E
+    stats = T * 4 * (2 if w.norm == "layernorm" else 1)
+    return w.t * T * h * E + (T * h * E if w.has_residual else 0) + params + 2 * T * h * E + stats
+
+
+def bwd_bytes(w, T):
+    E, h = w.elem_bytes, w.h
+    nstat = 2 if w.norm == "layernorm" else 1
+    return 3 * T * h * E + T * 4 * nstat + h * E + h * 4 * nstat
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in FWD_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per forward launch from the committed counter summary, or None
+    when missing or taken on a different kernel source."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, as it is, on a bounded sample of the workload.
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, inp, budget_s=12.0, chunk=64):
+    import numpy as np
+    import oracle.region as ref
+    T = inp["T"]
+    done, t0 = 0, time.perf_counter()
+    start = 0
+    while time.perf_counter() - t0 < budget_s:
+        rows = np.arange(start, min(T, start + chunk))
+        o = ref.region_forward(inp["partials"], t=w.t, rank=0, dtype=w.dtype, norm=w.norm, eps=w.eps,
+                               p_drop=w.p_drop, seed=inp["seed"], gamma=inp["gamma"], beta=inp["beta"],
+                               bias=inp["bias"], residual=inp["residual"], cu_seqlens=inp["cu_seqlens"], rows=rows)
+        ref.region_backward(inp["dy"][rows], o["z"], inp["gamma"], dtype=w.dtype, norm=w.norm, eps=w.eps)
+        done += len(rows)
+        start = (start + chunk) % T
+    el = time.perf_counter() - t0
+    return dict(value=done / el, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{done} rows of the {T}-row shard, cycled in chunks of {chunk} (forward + backward, "
+                       f"{el:.1f} s, single process: numpy element-wise ops on one core)")
+
+
+# ---------------------------------------------------------------------------
+def run(args):
+    import numpy as np
+    import torch
+    import layernorm_sp_region_amd as spr
+    import workloads as W
+
+    spr.load_library()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (the region has no CPU path)")
+    dev = torch.device("cuda:0")
+    w = W.BY_NAME[args.workload]
+    t_gen = time.time()
+    inp = W.make_inputs(w)
+    T, h = inp["T"], w.h
+    eprint(f"[bench] {w.name}: T={T} h={h} t={w.t} dtype={w.dtype} (inputs {time.time() - t_gen:.1f}s)")
+    tt = lambda a: W.as_torch(a, dev)
+
+    gamma, beta, bias = tt(inp["gamma"]), tt(inp["beta"]), tt(inp["bias"])
+    dt = gamma.dtype
+    sets = []
+    base = dict(P=tt(inp["partials"]), res=tt(inp["residual"]), dy=tt(inp["dy"]))
+    for i in range(args.sets):
+        s = {k: (v if i == 0 or v is None else v.clone()) for k, v in base.items()}
+        ln = w.norm == "layernorm"
+        s["fo"] = spr.FwdOut(torch.empty((T, h), dtype=dt, device=dev), torch.empty((T, h), dtype=dt, device=dev),
+                             torch.empty(T, device=dev) if ln else None, torch.empty(T, device=dev), None)
+        s["bo"] = spr.BwdOut(torch.empty((T, h), dtype=dt, device=dev), torch.empty(h, device=dev),
+                             torch.empty(h, device=dev) if ln else None)
+        sets.append(s)
+    ws = torch.empty(max(16, spr.workspace_bytes(T, h)), dtype=torch.uint8, device=dev)
+    cu = torch.tensor(inp["cu_seqlens"], dtype=torch.int32, device=dev) if inp["cu_seqlens"] is not None else None
+
+    def step(i, ev=None):
+        s = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record()
+        fo = spr.fwd(s["P"], gamma, beta, bias=bias, residual=s["res"], b=inp["b"], s=inp["s"], t=w.t, rank=0,
+                     eps=w.eps, p_drop=w.p_drop, seed=inp["seed"], norm=w.norm, cu_seqlens=cu, out=s["fo"])
+        if ev is not None:
+            ev[1].record()
+        spr.bwd(s["dy"], fo.z, fo.mean, fo.rstd, gamma, b=inp["b"], s=inp["s"], t=w.t, norm=w.norm,
+                workspace=ws, out=s["bo"])
+        if ev is not None:
+            ev[2].record()
+
+    # Copy-kernel ceiling on 1 GiB (also the reference for the traffic counters).
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(2):
+        spr.hbm_copy(src, dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        spr.hbm_copy(src, dst)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * nb * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    eprint(f"[bench] copy ceiling {copy_gbs:.0f} GB/s ({100 * copy_gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    fb, bb = fwd_bytes(w, T), bwd_bytes(w, T)
+    fwd_s = float(fwd_ms.mean()) * 1e-3
+    achieved = fb / fwd_s / 1e9
+    step_ms = elapsed / args.steps * 1e3
+    eprint(f"[bench] fwd {fwd_ms.mean() * 1e3:.1f} us (p50 {np.median(fwd_ms) * 1e3:.1f}), "
+           f"bwd {bwd_ms.mean() * 1e3:.1f} us, step {step_ms * 1e3:.1f} us wall; fwd {achieved:.0f} GB/s, "
+           f"fwd+bwd {(fb + bb) / ((fwd_ms.mean() + bwd_ms.mean()) * 1e-3) / 1e9:.0f} GB/s")
+
+    traffic = read_traffic()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp)
+    kernel_us = (fwd_ms.mean() + bwd_ms.mean()) * 1e3
+    rec = {
+        "metric": METRIC,
+        "value": T * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1)/sqrt(8) partial slabs, N(0,1) residual and dy, shaped like the pages' workloads)",
+        "config": {"workload": w.name, "s": inp["s"], "b": inp["b"], "h": h, "t": w.t, "local_tokens": T,
+                   "p_drop": w.p_drop, "norm": w.norm, "rank": 0, "rotating_sets": args.sets},
+        "fwd_us": float(fwd_ms.mean() * 1e3),
+        "bwd_us": float(bwd_ms.mean() * 1e3),
+        "fwd_bwd_hbm_gbs": (fb + bb) / (kernel_us * 1e-6) / 1e9,
+        "fwd_bwd_pct_of_peak": 100 * (fb + bb) / (kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_bytes": {"fwd": fb, "bwd": bb},
+        "copy_ceiling_gbs": copy_gbs,
+        "roofline": {"kernel": "sp_region_fwd_kernel", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 output -> short text summary (kernel stats or counters).
+# ---------------------------------------------------------------------------
+def summarize_rocprof(d):
+    out = []
+    stats = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    for p in stats:
+        out.append(f"# kernel stats: {os.path.relpath(p, d)}")
+        with open(p) as f:
+            rows = list(csv.DictReader(f))
+        for r in rows:
+            name = r.get("Name", "")[:90]
+            out.append(f"{name:90s} calls={r.get('Calls')} avg_ns={float(r.get('AverageNs', 0)):.0f} "
+                       f"min_ns={float(r.get('MinNs', 0)):.0f} max_ns={float(r.get('MaxNs', 0)):.0f} "
+                       f"pct={float(r.get('Percentage', 0)):.2f}")
+    counters = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    for p in counters:
+        out.append(f"# counters: {os.path.relpath(p, d)}")
+        agg = {}
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                key = (r.get("Kernel_Name", "")[:90], r.get("Counter_Name"))
+                agg.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
+        for (k, c), vals in sorted(agg.items()):
+            out.append(f"{k:90s} {c}: dispatches={len(vals)} mean_per_dispatch={sum(vals) / len(vals):.1f}")
+    print("\n".join(out))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="shard70b")
+    ap.add_argument("--sets", type=int, default=4, help="rotating input/output sets (Infinity Cache defeat)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-rocprof", metavar="DIR")
+    args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof)
+        return
+    if args.gpus != 1:
+        eprint(f"bench.py measures one GPU's shard; --gpus {args.gpus} is not supported "
+               "(this build runs on a single MI355X: no collectives, no multi-GPU launch)")
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

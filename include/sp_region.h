@@ -1,0 +1,175 @@
+/*
+ * sp_region.h -- C ABI of the fused sequence-parallel region for MI355X (gfx950).
+ *
+ * The region is the non-tensor-parallel part of a Megatron TP+SP transformer
+ * block, on one rank's sequence shard [s/t][b][h]:
+ *
+ *   forward   z = residual + dropout(sum_{k<t} P_k + bias)
+ *             y = LayerNorm(z) or RMSNorm(z), per token over the full h
+ *   backward  dx = dL/dz (+ dres_in), dgamma, dbeta
+ *
+ * P_k is this rank's [T][h] slice of TP rank k's row-parallel-linear partial
+ * output, so the sum is the arithmetic of the g* reduce-scatter done locally
+ * (hpc.payai.win lesson 7 "Sequence parallelism", section 3.A: g* sums the
+ * row-linear partial outputs and leaves each rank its s/t slice).  LayerNorm
+ * is the formula of section 2 of that lesson (mean and population variance
+ * over h, eps inside the square root, then gamma and beta).  Dropout masks
+ * are a pure function of (seed, global token, channel), so every rank draws
+ * the same mask for the same token, as the lesson's answer to question 1
+ * requires; the (b, s, h, t, eps, p, gamma, beta) argument set follows the
+ * lesson's statement of the problem.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers unless stated; `stream` is a hipStream_t
+ *     passed as void* (NULL = the default stream).
+ *   - T = b * s / t local rows; every [T][h] tensor is row-major, contiguous,
+ *     row i at element offset i*h.  A packed ragged batch is passed as b = 1
+ *     and s = total packed length, with cu_seqlens giving local row offsets.
+ *   - dtype SPR_BF16: activations, gamma, beta and bias are bfloat16;
+ *     SPR_F32: all float32.  mean, rstd, dgamma, dbeta are always float32.
+ *   - The caller owns every buffer (the backward workspace included).  The
+ *     library allocates nothing, keeps no mutable global state, launches
+ *     asynchronously on `stream`, never synchronises and never reads device
+ *     memory on the host.  Outputs are overwritten, not accumulated.
+ *   - Errors: a nonzero status is returned BEFORE any launch and leaves every
+ *     output untouched.  Argument checks: see each function.  A failed launch
+ *     returns SPR_ERR_HIP; sp_region_last_hip_error() then gives the raw
+ *     hipError_t of this thread.  Nothing prints, aborts or throws.
+ *   - Every device pointer must be 16-byte aligned.
+ */
+#ifndef SP_REGION_H_
+#define SP_REGION_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SP_REGION_ABI_VERSION 1
+
+enum sp_region_status {
+  SPR_OK = 0,
+  SPR_ERR_INVALID_ARG = 1,  /* argument outside its documented domain */
+  SPR_ERR_UNSUPPORTED = 2,  /* valid, but not compiled for (h, t, dtype) */
+  SPR_ERR_ALIGNMENT = 3,    /* pointer or slab stride not 16-byte aligned */
+  SPR_ERR_HIP = 4           /* kernel launch failed (see sp_region_last_hip_error) */
+};
+
+enum sp_region_dtype { SPR_F32 = 0, SPR_BF16 = 1 };
+enum sp_region_norm { SPR_LAYERNORM = 0, SPR_RMSNORM = 1 };
+
+/* Limits of the compiled kernels. */
+#define SPR_MAX_T_SLABS 8      /* tensor-parallel degree t: 1..8 */
+#define SPR_MAX_H_BF16 16384   /* h % 8 == 0 */
+#define SPR_MAX_H_F32 8192     /* h % 4 == 0 */
+
+/* Returns SP_REGION_ABI_VERSION of the built library. */
+int sp_region_abi_version(void);
+
+/* Static string naming a status code (never NULL). */
+const char* sp_region_strerror(int status);
+
+/* hipError_t of this thread's last SPR_ERR_HIP (0 if none). */
+int sp_region_last_hip_error(void);
+
+/*
+ * Forward of the region on one rank's shard.
+ *
+ *   b, s, t      micro-batch, global sequence length, TP degree (1..8);
+ *                s % t == 0; T = b*s/t.  Ragged: b must be 1.
+ *   h            hidden size; bf16: h % 8 == 0, h <= SPR_MAX_H_BF16;
+ *                f32: h % 4 == 0, h <= SPR_MAX_H_F32.
+ *   eps          > 0 and finite; added to the variance (LayerNorm) or to the
+ *                mean square (RMSNorm) inside the square root.
+ *   p_drop       dropout probability in [0, 1).  Element (i, j) is kept iff
+ *                word (j mod 4) of Philox-4x32-10(counter = (j div 4,
+ *                lo32 g_i, hi32 g_i, 0), key = (lo32 seed, hi32 seed)) is
+ *                >= floor(p_drop * 2^32); kept values are scaled by the
+ *                float32 value of 1/(1 - p_drop).  p_drop == 0 skips the hash.
+ *                (Philox: Salmon et al., "Parallel random numbers: as easy as
+ *                1, 2, 3", SC'11.)
+ *   gamma        [h], required.  beta: [h] or NULL (no shift); must be NULL
+ *                for RMSNorm.
+ *   norm, dtype  enum values above.
+ *   rank         this rank's index in the TP group, 0 <= rank < t.
+ *   seed         dropout seed, identical on every rank.
+ *   partials     t slabs, slab k at element offset k*slab_stride, each [T][h];
+ *                slab_stride >= T*h and slab_stride*elem_size % 16 == 0.
+ *   bias         [h] or NULL, added to the slab sum before dropout.
+ *   residual     [T][h] or NULL, added after dropout.
+ *   cu_seqlens   NULL for a uniform shard: the global token of local row i is
+ *                g_i = rank*T + i.  Otherwise int32 [nseq+1] local row offsets
+ *                (cu[0] = 0, cu[nseq] = T, non-decreasing; the caller
+ *                guarantees this, it is not checked on the device): row i of
+ *                sequence q has g_i = t*cu[q] + rank*(cu[q+1]-cu[q]) + (i-cu[q]).
+ *   z            out [T][h]: round_to_dtype(residual + dropout(sum + bias)),
+ *                summed in float32 in ascending k with no fused multiply-add.
+ *   y            out [T][h]: the normalised z (statistics from the rounded z).
+ *   mean, rstd   out float32 [T]; mean must be NULL for RMSNorm.
+ *   mask_out     NULL, or out uint8 [T][h] (1 = kept) for inspection.
+ *
+ * T == 0 is a no-op returning SPR_OK.
+ */
+int sp_region_fwd(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p_drop,
+                  const void* gamma, const void* beta,
+                  int32_t norm, int32_t dtype, int32_t rank, uint64_t seed,
+                  const void* partials, int64_t slab_stride,
+                  const void* bias, const void* residual,
+                  const int32_t* cu_seqlens, int32_t nseq,
+                  void* z, void* y, float* mean, float* rstd,
+                  uint8_t* mask_out,
+                  void* stream);
+
+/*
+ * Bytes of device workspace sp_region_bwd needs for n_local_tokens = T rows of
+ * h channels: a float32 [G][2][h] array of per-block dgamma/dbeta partial sums,
+ * G a fixed function of (T, h).  A pure function (no device query).  Returns 0
+ * for T <= 0 or h <= 0.
+ */
+size_t sp_region_bwd_workspace_bytes(int64_t n_local_tokens, int64_t h);
+
+/*
+ * Backward of the normalisation (the adjoint of the forward's last step).
+ *
+ *   b, s, t, h, norm, dtype   as in sp_region_fwd (T = b*s/t).
+ *   gamma        [h].
+ *   dy           [T][h] upstream gradient of y.
+ *   z            [T][h] the forward's z.
+ *   mean, rstd   the forward's float32 statistics (mean NULL for RMSNorm).
+ *   dres_in      [T][h] or NULL: extra gradient arriving on z (z is also the
+ *                next residual stream); added to dx.
+ *   dx           out [T][h]: with xhat = (z - mean)*rstd (RMS: z*rstd),
+ *                g = dy*gamma, c1 = mean_j g, c2 = mean_j(g*xhat):
+ *                LayerNorm dx = rstd*(g - c1 - xhat*c2) (+ dres_in),
+ *                RMSNorm   dx = rstd*(g - xhat*c2)      (+ dres_in).
+ *   dgamma       out float32 [h]: sum over this rank's T rows of dy*xhat.
+ *   dbeta        out float32 [h] or NULL: sum over the T rows of dy
+ *                (must be NULL for RMSNorm).
+ *   workspace    >= sp_region_bwd_workspace_bytes(T, h) bytes, 16-byte aligned
+ *                (may be NULL when that is 0).  Contents are scratch.
+ *
+ * dgamma/dbeta are reduced in a fixed order, so results are bitwise
+ * reproducible for a given (T, h).  T == 0 writes zeros to dgamma/dbeta.
+ */
+int sp_region_bwd(int64_t b, int64_t s, int64_t h, int32_t t,
+                  const void* gamma, int32_t norm, int32_t dtype,
+                  const void* dy, const void* z, const float* mean, const float* rstd,
+                  const void* dres_in,
+                  void* dx, float* dgamma, float* dbeta,
+                  void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
+ * Calibration kernel: copies nbytes (a multiple of 16) from src to dst with
+ * 16-byte loads and stores, for measuring the achievable HBM copy rate and for
+ * scaling hardware traffic counters.  Not part of the region's computation.
+ */
+int sp_region_hbm_copy(const void* src, void* dst, size_t nbytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SP_REGION_H_ */

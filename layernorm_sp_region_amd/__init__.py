@@ -1,0 +1,250 @@
+"""MI355X-native fused sequence-parallel region: Python binding of libsp_region.so.
+
+The sequence-parallel (non-TP) region of a Megatron TP+SP block on one rank's
+shard [s/t][b][h] (hpc.payai.win lesson 7 "Sequence parallelism"):
+
+    forward   z = residual + dropout(sum_k P_k + bias);  y = LayerNorm/RMSNorm(z)
+    backward  dx, dgamma, dbeta
+
+This module only marshals arguments: it checks torch tensors (device, dtype,
+shape, contiguity), allocates outputs with torch, and calls the C ABI
+(include/sp_region.h) on torch's current stream.  Every step of the
+computation runs in the library's HIP kernels.  If the library has not been
+built the calls raise; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from collections import namedtuple
+from typing import Optional, Sequence, Union
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsp_region.so")
+
+SPR_OK, SPR_ERR_INVALID_ARG, SPR_ERR_UNSUPPORTED, SPR_ERR_ALIGNMENT, SPR_ERR_HIP = range(5)
+SPR_F32, SPR_BF16 = 0, 1
+SPR_LAYERNORM, SPR_RMSNORM = 0, 1
+ABI_VERSION = 1
+
+# Every symbol include/sp_region.h declares, with its ctypes signature.
+_VP, _I64, _I32, _U64, _F32, _SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64,
+                                    ctypes.c_float, ctypes.c_size_t)
+SIGNATURES = {
+    "sp_region_abi_version": (ctypes.c_int, []),
+    "sp_region_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "sp_region_last_hip_error": (ctypes.c_int, []),
+    "sp_region_fwd": (ctypes.c_int, [_I64, _I64, _I64, _I32, _F32, _F32, _VP, _VP, _I32, _I32, _I32, _U64,
+                                     _VP, _I64, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "sp_region_bwd_workspace_bytes": (_SZ, [_I64, _I64]),
+    "sp_region_bwd": (ctypes.c_int, [_I64, _I64, _I64, _I32, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
+                                     _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "sp_region_hbm_copy": (ctypes.c_int, [_VP, _VP, _SZ, _VP]),
+}
+
+_lib = None
+
+
+def load_library(reload: bool = False):
+    """Load the in-tree libsp_region.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and not reload:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python __graft_entry__.py` "
+                          "(the region has no non-HIP implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.sp_region_abi_version() != ABI_VERSION:
+        raise ImportError(f"libsp_region ABI {lib.sp_region_abi_version()} != binding ABI {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+class SpRegionError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        lib = load_library()
+        msg = lib.sp_region_strerror(status).decode()
+        if status == SPR_ERR_HIP:
+            msg += f" (hipError_t {lib.sp_region_last_hip_error()})"
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+def _check(fn: str, status: int):
+    if status != SPR_OK:
+        raise SpRegionError(fn, status)
+
+
+FwdOut = namedtuple("FwdOut", "z y mean rstd mask")
+BwdOut = namedtuple("BwdOut", "dx dgamma dbeta")
+
+
+def _norm_code(norm: Union[str, int]) -> int:
+    if norm in ("layernorm", SPR_LAYERNORM):
+        return SPR_LAYERNORM
+    if norm in ("rmsnorm", SPR_RMSNORM):
+        return SPR_RMSNORM
+    raise ValueError(f"unknown norm {norm!r}")
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    if dt == torch.bfloat16:
+        return SPR_BF16
+    if dt == torch.float32:
+        return SPR_F32
+    raise TypeError(f"activations must be bfloat16 or float32, got {dt}")
+
+
+def _ptr(x) -> Optional[int]:
+    return None if x is None else x.data_ptr()
+
+
+def _require(x, name, device, dtype=None, shape=None):
+    if x is None:
+        return
+    if not x.is_cuda or x.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if dtype is not None and x.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {x.dtype}")
+    if shape is not None and tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(x.shape)}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def local_tokens(b: int, s: int, t: int) -> int:
+    return b * s // t
+
+
+def check_cu_seqlens(cu: Sequence[int], T: int) -> None:
+    """Host check of the packed-batch offsets (the kernels trust them)."""
+    cu = [int(x) for x in cu]
+    if len(cu) < 2 or cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must start at 0, end at T and be non-decreasing")
+
+
+def fwd(partials, gamma, beta=None, *, bias=None, residual=None, b: int, s: int, t: int, rank: int,
+        eps: float, p_drop: float, seed: int, norm: Union[str, int] = "layernorm", cu_seqlens=None,
+        return_mask: bool = False, out: Optional[FwdOut] = None) -> FwdOut:
+    """Forward of the region.
+
+    partials: [t][T][h] tensor (slab k = partials[k]; each slab row-major; the
+    slab stride may exceed T*h).  cu_seqlens: None (uniform shard) or the
+    host list / CPU tensor / int32 CUDA tensor of local row offsets of a packed
+    batch (b must be 1; a CUDA tensor is trusted as-is).  `out` may supply
+    preallocated outputs.  Returns FwdOut(z, y, mean, rstd, mask).
+    """
+    import torch
+    lib = load_library()
+    nc = _norm_code(norm)
+    dev = partials.device
+    dt = partials.dtype
+    dcode = _dtype_code(dt)
+    if partials.dim() != 3 or partials.shape[0] != t:
+        raise ValueError(f"partials must be [t={t}][T][h], got {tuple(partials.shape)}")
+    _, T, h = partials.shape
+    if T != local_tokens(b, s, t):
+        raise ValueError(f"partials hold {T} rows, expected b*s/t = {local_tokens(b, s, t)}")
+    if partials.stride(2) != 1 or partials.stride(1) != h:
+        raise ValueError("each slab of partials must be row-major contiguous")
+    if not partials.is_cuda:
+        raise ValueError("partials must be a CUDA tensor")
+    _require(gamma, "gamma", dev, dt, (h,))
+    _require(beta, "beta", dev, dt, (h,))
+    _require(bias, "bias", dev, dt, (h,))
+    _require(residual, "residual", dev, dt, (T, h))
+    nseq = 0
+    cu_dev = None
+    if cu_seqlens is not None:
+        if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
+            _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
+            cu_dev = cu_seqlens
+        else:
+            cu_list = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+            check_cu_seqlens(cu_list, T)
+            cu_dev = torch.tensor(cu_list, dtype=torch.int32, device=dev)
+        nseq = cu_dev.numel() - 1
+    ln = nc == SPR_LAYERNORM
+    if out is None:
+        z = torch.empty((T, h), dtype=dt, device=dev)
+        y = torch.empty((T, h), dtype=dt, device=dev)
+        mean = torch.empty((T,), dtype=torch.float32, device=dev) if ln else None
+        rstd = torch.empty((T,), dtype=torch.float32, device=dev)
+        mask = torch.empty((T, h), dtype=torch.uint8, device=dev) if return_mask else None
+    else:
+        z, y, mean, rstd, mask = out
+        _require(z, "z", dev, dt, (T, h))
+        _require(y, "y", dev, dt, (T, h))
+        _require(mean, "mean", dev, torch.float32, (T,))
+        _require(rstd, "rstd", dev, torch.float32, (T,))
+        _require(mask, "mask", dev, torch.uint8, (T, h))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.sp_region_fwd(b, s, h, t, float(eps), float(p_drop), _ptr(gamma), _ptr(beta), nc, dcode, rank,
+                           int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(partials), partials.stride(0), _ptr(bias),
+                           _ptr(residual), _ptr(cu_dev), nseq, _ptr(z), _ptr(y), _ptr(mean), _ptr(rstd),
+                           _ptr(mask), stream)
+    _check("sp_region_fwd", st)
+    return FwdOut(z, y, mean, rstd, mask)
+
+
+def workspace_bytes(T: int, h: int) -> int:
+    return int(load_library().sp_region_bwd_workspace_bytes(T, h))
+
+
+def bwd(dy, z, mean, rstd, gamma, *, b: int, s: int, t: int, norm: Union[str, int] = "layernorm",
+        dres_in=None, want_dbeta: bool = True, workspace=None, out: Optional[BwdOut] = None) -> BwdOut:
+    """Backward of the region's normalisation.  Returns BwdOut(dx, dgamma, dbeta)
+    (dbeta None for RMSNorm or when want_dbeta is False)."""
+    import torch
+    lib = load_library()
+    nc = _norm_code(norm)
+    dev = z.device
+    dt = z.dtype
+    dcode = _dtype_code(dt)
+    T, h = z.shape
+    if T != local_tokens(b, s, t):
+        raise ValueError(f"z holds {T} rows, expected b*s/t = {local_tokens(b, s, t)}")
+    ln = nc == SPR_LAYERNORM
+    _require(z, "z", dev, dt, (T, h))
+    _require(dy, "dy", dev, dt, (T, h))
+    _require(dres_in, "dres_in", dev, dt, (T, h))
+    _require(gamma, "gamma", dev, dt, (h,))
+    _require(mean, "mean", dev, torch.float32, (T,))
+    _require(rstd, "rstd", dev, torch.float32, (T,))
+    if ln and mean is None:
+        raise ValueError("LayerNorm backward needs mean")
+    need = workspace_bytes(T, h)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _require(workspace, "workspace", dev, torch.uint8)
+    if out is None:
+        dx = torch.empty((T, h), dtype=dt, device=dev)
+        dgamma = torch.empty((h,), dtype=torch.float32, device=dev)
+        dbeta = torch.empty((h,), dtype=torch.float32, device=dev) if (ln and want_dbeta) else None
+    else:
+        dx, dgamma, dbeta = out
+        _require(dx, "dx", dev, dt, (T, h))
+        _require(dgamma, "dgamma", dev, torch.float32, (h,))
+        _require(dbeta, "dbeta", dev, torch.float32, (h,))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.sp_region_bwd(b, s, h, t, _ptr(gamma), nc, dcode, _ptr(dy), _ptr(z), _ptr(mean if ln else None),
+                           _ptr(rstd), _ptr(dres_in), _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(workspace),
+                           workspace.numel(), stream)
+    _check("sp_region_bwd", st)
+    return BwdOut(dx, dgamma, dbeta)
+
+
+def hbm_copy(src, dst) -> None:
+    """Calibration copy of src's bytes into dst (same size, 16-byte multiple)."""
+    import torch
+    lib = load_library()
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst sizes differ")
+    stream = torch.cuda.current_stream(src.device).cuda_stream
+    _check("sp_region_hbm_copy", lib.sp_region_hbm_copy(src.data_ptr(), dst.data_ptr(), n, stream))

@@ -1,0 +1,175 @@
+// C ABI of the SP-region library: argument validation, then dispatch to the
+// kernel launchers.  Every check runs before any HIP call, so an invalid call
+// launches nothing and leaves the outputs untouched.
+#include <cmath>
+#include <cstdint>
+
+#include "sp_region.h"
+#include "spr_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned16_or_null(const void* p) { return p == nullptr || aligned16(p); }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return SPR_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return SPR_ERR_HIP;
+}
+
+// Shared shape checks of fwd and bwd; on success sets T.
+int check_shape(int64_t b, int64_t s, int64_t h, int32_t t, int32_t norm, int32_t dtype, int64_t* T) {
+  if (t < 1 || b < 1 || s < 0 || h <= 0) return SPR_ERR_INVALID_ARG;
+  if (dtype != SPR_F32 && dtype != SPR_BF16) return SPR_ERR_INVALID_ARG;
+  if (norm != SPR_LAYERNORM && norm != SPR_RMSNORM) return SPR_ERR_INVALID_ARG;
+  if (s % t != 0) return SPR_ERR_INVALID_ARG;
+  if (t > SPR_MAX_T_SLABS) return SPR_ERR_UNSUPPORTED;
+  const int64_t vec = dtype == SPR_BF16 ? 8 : 4;
+  const int64_t hmax = dtype == SPR_BF16 ? SPR_MAX_H_BF16 : SPR_MAX_H_F32;
+  if (h % vec != 0 || h > hmax) return SPR_ERR_UNSUPPORTED;
+  const int64_t per_rank = s / t;
+  if (per_rank > 0 && b > INT64_MAX / per_rank) return SPR_ERR_INVALID_ARG;
+  *T = b * per_rank;
+  if (*T > INT32_MAX) return SPR_ERR_UNSUPPORTED;   // grid.x limit of one row per block
+  return SPR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sp_region_abi_version(void) { return SP_REGION_ABI_VERSION; }
+
+const char* sp_region_strerror(int status) {
+  switch (status) {
+    case SPR_OK: return "ok";
+    case SPR_ERR_INVALID_ARG: return "invalid argument";
+    case SPR_ERR_UNSUPPORTED: return "unsupported shape (t, h or dtype outside the compiled kernels)";
+    case SPR_ERR_ALIGNMENT: return "pointer or slab stride not 16-byte aligned";
+    case SPR_ERR_HIP: return "HIP launch error (see sp_region_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int sp_region_last_hip_error(void) { return g_last_hip_error; }
+
+int sp_region_fwd(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p_drop,
+                  const void* gamma, const void* beta,
+                  int32_t norm, int32_t dtype, int32_t rank, uint64_t seed,
+                  const void* partials, int64_t slab_stride,
+                  const void* bias, const void* residual,
+                  const int32_t* cu_seqlens, int32_t nseq,
+                  void* z, void* y, float* mean, float* rstd,
+                  uint8_t* mask_out,
+                  void* stream) {
+  int64_t T = 0;
+  int st = check_shape(b, s, h, t, norm, dtype, &T);
+  if (st != SPR_OK) return st;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return SPR_ERR_INVALID_ARG;
+  if (!(p_drop >= 0.0f && p_drop < 1.0f)) return SPR_ERR_INVALID_ARG;
+  if (rank < 0 || rank >= t) return SPR_ERR_INVALID_ARG;
+  if (cu_seqlens != nullptr && (nseq < 1 || b != 1)) return SPR_ERR_INVALID_ARG;
+  if (nseq < 0) return SPR_ERR_INVALID_ARG;
+  if (T == 0) return SPR_OK;
+  const bool ln = norm == SPR_LAYERNORM;
+  if (!partials || !gamma || !z || !y || !rstd) return SPR_ERR_INVALID_ARG;
+  if (ln != (mean != nullptr)) return SPR_ERR_INVALID_ARG;
+  if (!ln && beta != nullptr) return SPR_ERR_INVALID_ARG;
+  if (slab_stride < T * h) return SPR_ERR_INVALID_ARG;
+  const int64_t eb = dtype == SPR_BF16 ? 2 : 4;
+  if ((slab_stride * eb) % 16 != 0) return SPR_ERR_ALIGNMENT;
+  for (const void* ptr : {partials, gamma, static_cast<const void*>(z), static_cast<const void*>(y),
+                          static_cast<const void*>(rstd)})
+    if (!aligned16(ptr)) return SPR_ERR_ALIGNMENT;
+  for (const void* ptr : {beta, bias, residual, static_cast<const void*>(mean), static_cast<const void*>(mask_out)})
+    if (!aligned16_or_null(ptr)) return SPR_ERR_ALIGNMENT;
+  if (cu_seqlens != nullptr && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return SPR_ERR_ALIGNMENT;
+
+  spr::FwdParams p{};
+  p.partials = partials;
+  p.slab_stride = slab_stride;
+  p.bias = bias;
+  p.residual = residual;
+  p.gamma = gamma;
+  p.beta = beta;
+  p.cu = cu_seqlens;
+  p.nseq = nseq;
+  p.z = z;
+  p.y = y;
+  p.mean = mean;
+  p.rstd = rstd;
+  p.mask = mask_out;
+  p.T = T;
+  p.h = static_cast<int32_t>(h);
+  p.t = t;
+  p.rank = rank;
+  p.norm = norm;
+  p.eps = eps;
+  const double pd = static_cast<double>(p_drop);
+  p.drop = p_drop > 0.0f ? 1 : 0;
+  p.scale = static_cast<float>(1.0 / (1.0 - pd));
+  p.thr = static_cast<uint32_t>(std::floor(pd * 4294967296.0));
+  p.key0 = static_cast<uint32_t>(seed);
+  p.key1 = static_cast<uint32_t>(seed >> 32);
+  return hip_status(spr::launch_fwd(p, dtype, static_cast<hipStream_t>(stream)));
+}
+
+size_t sp_region_bwd_workspace_bytes(int64_t n_local_tokens, int64_t h) {
+  if (n_local_tokens <= 0 || h <= 0) return 0;
+  return static_cast<size_t>(spr::bwd_blocks(n_local_tokens, h)) * 2u * static_cast<size_t>(h) * sizeof(float);
+}
+
+int sp_region_bwd(int64_t b, int64_t s, int64_t h, int32_t t,
+                  const void* gamma, int32_t norm, int32_t dtype,
+                  const void* dy, const void* z, const float* mean, const float* rstd,
+                  const void* dres_in,
+                  void* dx, float* dgamma, float* dbeta,
+                  void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  int64_t T = 0;
+  int st = check_shape(b, s, h, t, norm, dtype, &T);
+  if (st != SPR_OK) return st;
+  const bool ln = norm == SPR_LAYERNORM;
+  if (!gamma || !dgamma) return SPR_ERR_INVALID_ARG;
+  if (!ln && dbeta != nullptr) return SPR_ERR_INVALID_ARG;
+  const size_t need = sp_region_bwd_workspace_bytes(T, h);
+  if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return SPR_ERR_INVALID_ARG;
+  if (T > 0) {
+    if (!dy || !z || !rstd || !dx) return SPR_ERR_INVALID_ARG;
+    if (ln != (mean != nullptr)) return SPR_ERR_INVALID_ARG;
+  }
+  for (const void* ptr : {gamma, dy, z, static_cast<const void*>(mean), static_cast<const void*>(rstd), dres_in,
+                          static_cast<const void*>(dx), static_cast<const void*>(dgamma),
+                          static_cast<const void*>(dbeta), static_cast<const void*>(workspace)})
+    if (!aligned16_or_null(ptr)) return SPR_ERR_ALIGNMENT;
+
+  spr::BwdParams p{};
+  p.dy = dy;
+  p.z = z;
+  p.mean = mean;
+  p.rstd = rstd;
+  p.gamma = gamma;
+  p.dres = dres_in;
+  p.dx = dx;
+  p.ws = static_cast<float*>(workspace);
+  p.dgamma = dgamma;
+  p.dbeta = dbeta;
+  p.T = T;
+  p.h = static_cast<int32_t>(h);
+  p.norm = norm;
+  p.G = static_cast<int32_t>(spr::bwd_blocks(T, h));
+  return hip_status(spr::launch_bwd(p, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int sp_region_hbm_copy(const void* src, void* dst, size_t nbytes, void* stream) {
+  if (nbytes % 16 != 0) return SPR_ERR_INVALID_ARG;
+  if (nbytes == 0) return SPR_OK;
+  if (!src || !dst) return SPR_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(dst)) return SPR_ERR_ALIGNMENT;
+  return hip_status(spr::launch_copy(src, dst, nbytes, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Host-side contract between the C ABI (abi.cpp) and the kernel TUs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spr {
+
+// Parameters of one forward launch (validated by the ABI layer).
+struct FwdParams {
+  const void* partials;   // t slabs of [T][h]
+  int64_t slab_stride;    // elements between slabs
+  const void* bias;       // [h] or null
+  const void* residual;   // [T][h] or null
+  const void* gamma;      // [h]
+  const void* beta;       // [h] or null
+  const int32_t* cu;      // [nseq+1] local offsets or null (uniform shard)
+  int32_t nseq;
+  void* z;                // [T][h]
+  void* y;                // [T][h]
+  float* mean;            // [T] or null (RMSNorm)
+  float* rstd;            // [T]
+  uint8_t* mask;          // [T][h] or null
+  int64_t T;
+  int32_t h;
+  int32_t t;
+  int32_t rank;
+  int32_t norm;           // 0 LayerNorm, 1 RMSNorm
+  float eps;
+  float scale;            // float32(1/(1-p))
+  uint32_t thr;           // floor(p * 2^32); dropout active iff drop != 0
+  int32_t drop;
+  uint32_t key0, key1;    // lo32 / hi32 of the seed
+};
+
+struct BwdParams {
+  const void* dy;
+  const void* z;
+  const float* mean;      // null for RMSNorm
+  const float* rstd;
+  const void* gamma;
+  const void* dres;       // [T][h] or null
+  void* dx;
+  float* ws;              // [G][2][h]
+  float* dgamma;
+  float* dbeta;           // null allowed
+  int64_t T;
+  int32_t h;
+  int32_t norm;
+  int32_t G;
+};
+
+// Number of row blocks of the backward's first stage (and of workspace
+// partials): a pure function of (T, h) so the workspace size is known
+// without a device query.  256 = one block per MI355X compute unit.
+constexpr int kBwdMaxBlocks = 256;
+inline int64_t bwd_blocks(int64_t T, int64_t /*h*/) { return T < kBwdMaxBlocks ? T : kBwdMaxBlocks; }
+
+// Launchers: return hipSuccess or the launch error.  `dtype` 0 = f32, 1 = bf16.
+hipError_t launch_fwd(const FwdParams& p, int dtype, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int dtype, hipStream_t stream);
+hipError_t launch_copy(const void* src, void* dst, size_t nbytes, hipStream_t stream);
+
+// Launch shapes (exposed for tests of the host logic).
+struct Shape {
+  int vpt;      // 16-byte vectors per thread per row
+  int threads;  // block size, a multiple of 64
+};
+Shape fwd_shape(int h, int dtype);
+Shape bwd_shape(int h, int dtype);
+
+}  // namespace spr

@@ -1,0 +1,167 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function include/sp_region.h declares, and rejects invalid arguments with the
+documented status before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import layernorm_sp_region_amd as spr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sp_region.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sp_region_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(spr.LIB_PATH):
+        pytest.skip("library not built (run __graft_entry__.build())")
+    return spr.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(spr.SIGNATURES)
+    for required in ("sp_region_fwd", "sp_region_bwd", "sp_region_bwd_workspace_bytes", "sp_region_strerror",
+                     "sp_region_abi_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", spr.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (sp_region_\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+    for name in declared_functions():
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_strerror(lib):
+    assert lib.sp_region_abi_version() == spr.ABI_VERSION == 1
+    for st in range(5):
+        assert lib.sp_region_strerror(st)
+    assert lib.sp_region_strerror(99) == b"unknown status"
+    assert lib.sp_region_last_hip_error() == 0
+
+
+def test_workspace_bytes_is_pure(lib):
+    ws = lib.sp_region_bwd_workspace_bytes
+    assert ws(0, 8192) == 0 and ws(10, 0) == 0 and ws(-1, 8) == 0
+    assert ws(2048, 8192) == 256 * 2 * 8192 * 4       # one partial per block, 256 blocks
+    assert ws(64, 512) == 64 * 2 * 512 * 4            # T < 256: one row per block
+    assert ws(16384, 8192) == ws(2048, 8192)
+
+
+# A fake, well-aligned "device" address: validation only looks at its value.
+P = 0x10000
+
+
+def fwd_args(**over):
+    a = dict(b=1, s=256, h=512, t=4, eps=1e-5, p=0.1, gamma=P, beta=P, norm=0, dtype=0, rank=0, seed=1,
+             partials=P, slab_stride=64 * 512, bias=None, residual=P, cu=None, nseq=0, z=P, y=P, mean=P, rstd=P,
+             mask=None, stream=None)
+    a.update(over)
+    return a
+
+
+def call_fwd(lib, a):
+    return lib.sp_region_fwd(a["b"], a["s"], a["h"], a["t"], a["eps"], a["p"], a["gamma"], a["beta"], a["norm"],
+                             a["dtype"], a["rank"], a["seed"], a["partials"], a["slab_stride"], a["bias"],
+                             a["residual"], a["cu"], a["nseq"], a["z"], a["y"], a["mean"], a["rstd"], a["mask"],
+                             a["stream"])
+
+
+INVALID, UNSUP, ALIGN = spr.SPR_ERR_INVALID_ARG, spr.SPR_ERR_UNSUPPORTED, spr.SPR_ERR_ALIGNMENT
+
+FWD_CASES = [
+    (dict(p=1.0), INVALID), (dict(p=-0.1), INVALID), (dict(p=float("nan")), INVALID),
+    (dict(eps=0.0), INVALID), (dict(eps=-1e-5), INVALID), (dict(eps=float("inf")), INVALID),
+    (dict(s=258), INVALID),                       # s % t != 0
+    (dict(rank=4), INVALID), (dict(rank=-1), INVALID),
+    (dict(t=0), INVALID), (dict(t=9, s=252 * 9, rank=0), UNSUP),
+    (dict(b=0), INVALID), (dict(h=0), INVALID), (dict(s=-4), INVALID),
+    (dict(norm=2), INVALID), (dict(dtype=7), INVALID),
+    (dict(h=514), UNSUP),                         # f32 needs h % 4 == 0
+    (dict(dtype=1, h=516), UNSUP),                # bf16 needs h % 8 == 0
+    (dict(h=8196), UNSUP),                        # above SPR_MAX_H_F32
+    (dict(dtype=1, h=16392, slab_stride=64 * 16392), UNSUP),
+    (dict(partials=None), INVALID), (dict(gamma=None), INVALID), (dict(z=None), INVALID),
+    (dict(y=None), INVALID), (dict(rstd=None), INVALID), (dict(mean=None), INVALID),
+    (dict(norm=1, beta=None), INVALID),           # RMSNorm must not get mean
+    (dict(norm=1, mean=None), INVALID),           # ... nor beta
+    (dict(slab_stride=64 * 512 - 4), INVALID),    # slabs overlap
+    (dict(slab_stride=64 * 512 + 2), ALIGN),      # slab starts not 16-byte aligned
+    (dict(partials=P + 4), ALIGN), (dict(z=P + 8), ALIGN), (dict(residual=P + 2), ALIGN),
+    (dict(mask=P + 1), ALIGN), (dict(mean=P + 4), ALIGN), (dict(bias=P + 4), ALIGN),
+    (dict(cu=P, nseq=0), INVALID),                # ragged needs nseq >= 1
+    (dict(cu=P, nseq=2, b=2, s=128), INVALID),    # ragged needs b == 1
+    (dict(cu=P + 2, nseq=2), ALIGN),
+    (dict(nseq=-1), INVALID),
+]
+
+
+@pytest.mark.parametrize("over,status", FWD_CASES, ids=[str(c[0]) for c in FWD_CASES])
+def test_fwd_rejects(lib, over, status):
+    assert call_fwd(lib, fwd_args(**over)) == status
+
+
+def test_fwd_empty_shard_is_noop(lib):
+    # T == 0: OK without touching any pointer (all NULL).
+    a = fwd_args(s=0, partials=None, gamma=None, beta=None, residual=None, z=None, y=None, mean=None, rstd=None)
+    assert call_fwd(lib, a) == spr.SPR_OK
+
+
+def bwd_args(**over):
+    a = dict(b=1, s=256, h=512, t=4, gamma=P, norm=0, dtype=0, dy=P, z=P, mean=P, rstd=P, dres=None, dx=P,
+             dgamma=P, dbeta=P, ws=P, ws_bytes=64 * 2 * 512 * 4, stream=None)
+    a.update(over)
+    return a
+
+
+def call_bwd(lib, a):
+    return lib.sp_region_bwd(a["b"], a["s"], a["h"], a["t"], a["gamma"], a["norm"], a["dtype"], a["dy"], a["z"],
+                             a["mean"], a["rstd"], a["dres"], a["dx"], a["dgamma"], a["dbeta"], a["ws"],
+                             a["ws_bytes"], a["stream"])
+
+
+BWD_CASES = [
+    (dict(ws_bytes=64 * 2 * 512 * 4 - 1), INVALID), (dict(ws=None), INVALID),
+    (dict(dy=None), INVALID), (dict(z=None), INVALID), (dict(rstd=None), INVALID), (dict(dx=None), INVALID),
+    (dict(dgamma=None), INVALID), (dict(gamma=None), INVALID), (dict(mean=None), INVALID),
+    (dict(norm=1, dbeta=P, mean=None), INVALID), (dict(norm=1, mean=P, dbeta=None), INVALID),
+    (dict(s=257), INVALID), (dict(t=0), INVALID), (dict(h=510), UNSUP), (dict(dtype=2), INVALID),
+    (dict(dx=P + 4), ALIGN), (dict(ws=P + 8), ALIGN), (dict(dres=P + 2), ALIGN), (dict(dgamma=P + 4), ALIGN),
+]
+
+
+@pytest.mark.parametrize("over,status", BWD_CASES, ids=[str(c[0]) for c in BWD_CASES])
+def test_bwd_rejects(lib, over, status):
+    assert call_bwd(lib, bwd_args(**over)) == status
+
+
+def test_copy_rejects(lib):
+    assert lib.sp_region_hbm_copy(P, P, 15, None) == INVALID
+    assert lib.sp_region_hbm_copy(None, P, 16, None) == INVALID
+    assert lib.sp_region_hbm_copy(P + 4, P, 16, None) == ALIGN
+    assert lib.sp_region_hbm_copy(None, None, 0, None) == spr.SPR_OK
+
+
+def test_python_layer_checks_cu_seqlens():
+    spr.check_cu_seqlens([0, 3, 3, 8], 8)
+    for bad, T in (([1, 8], 8), ([0, 5, 4, 8], 8), ([0, 7], 8), ([0], 0)):
+        with pytest.raises(ValueError):
+            spr.check_cu_seqlens(bad, T)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(spr, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(spr, "_lib", None)
+    with pytest.raises(ImportError):
+        spr.load_library()

@@ -55,17 +55,21 @@ class Workload:
     nseq: int = 0         # ragged: number of packed sequences
     mean_len: float = 0.0  # ragged: arithmetic mean of the global lengths
     len_cv: float = 0.0    # ragged: std/mean of the global lengths
+    fixed_lengths: tuple = ()  # ragged: explicit global lengths (multiples of t, zeros allowed)
+    seed_override: int = -1    # custom cases: input seed (else 1000 + index)
 
     @property
     def ragged(self) -> bool:
-        return self.nseq > 0
+        return self.nseq > 0 or len(self.fixed_lengths) > 0
 
     @property
     def input_seed(self) -> int:
-        return 1000 + self.index
+        return self.seed_override if self.seed_override >= 0 else 1000 + self.index
 
     @property
     def dropout_seed(self) -> int:
+        if self.seed_override >= 0:      # custom cases: a seed with both 32-bit halves set
+            return 0x9E3779B97F4A7C15 ^ self.seed_override
         return 0x5EED0000 + self.index
 
     @property
@@ -98,7 +102,11 @@ BY_NAME = {w.name: w for w in WORKLOADS}
 def ragged_lengths(rng: np.random.Generator, w: Workload) -> np.ndarray:
     """Global lengths of the packed sequences: lognormal with the stated
     arithmetic mean and coefficient of variation, rounded to multiples of t
-    (half-to-even) and at least t."""
+    (half-to-even) and at least t.  Explicit lengths are returned as given."""
+    if w.fixed_lengths:
+        lens = np.asarray(w.fixed_lengths, dtype=np.int64)
+        assert np.all(lens % w.t == 0) and np.all(lens >= 0)
+        return lens
     sigma_ln = math.sqrt(math.log1p(w.len_cv ** 2))
     mu_ln = math.log(w.mean_len) - 0.5 * sigma_ln ** 2
     x = rng.lognormal(mean=mu_ln, sigma=sigma_ln, size=w.nseq)
@@ -135,11 +143,22 @@ def shard_geometry(w: Workload, lengths: Optional[np.ndarray] = None):
     if w.ragged:
         assert lengths is not None
         local = lengths // w.t
-        cu = np.zeros(w.nseq + 1, dtype=np.int32)
+        cu = np.zeros(len(lengths) + 1, dtype=np.int32)
         cu[1:] = np.cumsum(local)
         s = int(lengths.sum())
         return 1, s, int(cu[-1]), cu
     return w.b, w.s, w.b * w.s // w.t, None
+
+
+def custom(name: str, *, h: int, t: int, dtype: str = DTYPE_BF16, norm: str = LAYERNORM, eps: float = 1e-5,
+           p_drop: float = 0.1, bias: bool = True, residual: bool = True, beta: Optional[bool] = None,
+           s: int = 0, b: int = 1, lengths: tuple = (), seed: int = 7, slab_scale: float = _INV_SQRT8) -> Workload:
+    """An edge-case shard (odd t, ragged vector tails, empty sequences, ...)."""
+    if beta is None:
+        beta = norm == LAYERNORM
+    return Workload(name, -1, h=h, t=t, dtype=dtype, norm=norm, eps=eps, p_drop=p_drop, has_bias=bias,
+                    has_residual=residual, has_beta=beta, slab_scale=slab_scale, s=s, b=b,
+                    fixed_lengths=tuple(lengths), seed_override=seed)
 
 
 def make_inputs(w: Workload, seed: Optional[int] = None, with_dy: bool = True) -> Dict:
