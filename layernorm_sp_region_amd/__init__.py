@@ -150,10 +150,13 @@ def fwd(partials, gamma, beta=None, *, bias=None, residual=None, b: int, s: int,
     _, T, h = partials.shape
     if T != local_tokens(b, s, t):
         raise ValueError(f"partials hold {T} rows, expected b*s/t = {local_tokens(b, s, t)}")
-    if partials.stride(2) != 1 or partials.stride(1) != h:
-        raise ValueError("each slab of partials must be row-major contiguous")
-    if not partials.is_cuda:
+    if not partials.is_cuda or partials.device != dev:
         raise ValueError("partials must be a CUDA tensor")
+    # Strides of size-0/1 dims carry no layout information (numpy gives an
+    # inserted axis stride 0), so only meaningful ones are checked.
+    if T > 0 and ((h > 1 and partials.stride(2) != 1) or (T > 1 and partials.stride(1) != h)):
+        raise ValueError("each slab of partials must be row-major contiguous")
+    slab_stride = partials.stride(0) if t > 1 else T * h
     _require(gamma, "gamma", dev, dt, (h,))
     _require(beta, "beta", dev, dt, (h,))
     _require(bias, "bias", dev, dt, (h,))
@@ -185,7 +188,7 @@ def fwd(partials, gamma, beta=None, *, bias=None, residual=None, b: int, s: int,
         _require(mask, "mask", dev, torch.uint8, (T, h))
     stream = torch.cuda.current_stream(dev).cuda_stream
     st = lib.sp_region_fwd(b, s, h, t, float(eps), float(p_drop), _ptr(gamma), _ptr(beta), nc, dcode, rank,
-                           int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(partials), partials.stride(0), _ptr(bias),
+                           int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(partials), slab_stride, _ptr(bias),
                            _ptr(residual), _ptr(cu_dev), nseq, _ptr(z), _ptr(y), _ptr(mean), _ptr(rstd),
                            _ptr(mask), stream)
     _check("sp_region_fwd", st)

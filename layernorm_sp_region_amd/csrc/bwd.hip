@@ -9,8 +9,9 @@
 // Stage 1 (sp_region_bwd_rows_kernel): G blocks, block b owns the contiguous
 // rows [b*T/G, (b+1)*T/G).  Each thread owns a fixed set of columns, keeps
 // their gamma and their dgamma/dbeta running sums in registers across rows,
-// and the block writes one [2][h] float32 partial to the workspace.  RPI rows
-// are loaded together and their 2*RPI row sums share one block reduction.
+// and the block writes one [2][h] float32 partial to the workspace.  Rows
+// stream through a ring of RING packed row buffers (RING rows in flight per
+// block); each row's two sums take one block reduction.
 //
 // Stage 2 (sp_region_bwd_cols_kernel): dgamma/dbeta = the G partials summed in
 // ascending block order, split over 16 groups whose sums are combined in
@@ -21,19 +22,29 @@
 namespace spr {
 namespace {
 
-template <class E, int VPT, int RPI, int MAXBS>
+// Packed loads of one row: VPT vectors of dy, z (and dres) per thread.
+// The row's statistics travel with its data: every lane loads the same
+// mean/rstd (one broadcast request per wave), so waiting for a ring slot
+// never waits on loads issued after it (vmcnt completes in issue order).
+template <int VPT, bool DRES>
+struct RowBuf {
+  u32x4 dy[VPT], z[VPT], dr[DRES ? VPT : 1];
+  float mu, rs;
+};
+
+template <class E, int VPT, int RING, bool DRES, int MAXBS>
 __global__ __launch_bounds__(MAXBS) void sp_region_bwd_rows_kernel(const BwdParams p) {
   constexpr int V = E::kVec;
   constexpr int EB = 16 / V;
-  constexpr int NR = 2 * RPI;
-  __shared__ float red[2][NR * 16];
+  __shared__ float red[2][2 * 16];
 
   const int tid = threadIdx.x;
   const int bs = blockDim.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave, nwaves = bs / kWave;
   const int h = p.h;
   const int nvec = h / V;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * p.T / p.G;
-  const int64_t r1 = static_cast<int64_t>(blockIdx.x + 1) * p.T / p.G;
+  const int r0 = static_cast<int>(static_cast<int64_t>(blockIdx.x) * p.T / p.G);
+  const int r1 = static_cast<int>(static_cast<int64_t>(blockIdx.x + 1) * p.T / p.G);
   const bool ln = p.norm == 0;
   const float inv_h = 1.0f / static_cast<float>(h);
 
@@ -44,83 +55,106 @@ __global__ __launch_bounds__(MAXBS) void sp_region_bwd_rows_kernel(const BwdPara
   for (int k = 0; k < VPT; ++k) {
     const int v = tid + k * bs;
     valid[k] = v < nvec;
-    vv[k] = valid[k] ? v : nvec - 1;
+    vv[k] = valid[k] ? v : nvec - 1;   // clamped: loads stay in bounds
     unpack(E{}, ld16(static_cast<const char*>(p.gamma) + vv[k] * 16), gam[k]);
 #pragma unroll
     for (int e = 0; e < V; ++e) dg[k][e] = db[k][e] = 0.0f;
   }
 
+  // Rows stream through a ring of RING row buffers: row r + RING is issued
+  // as soon as row r has been consumed, so RING rows stay in flight.  The
+  // loads are unconditional (no branch for the waitcnt pass to merge over,
+  // which would force it to drain every outstanding load): past the block's
+  // last row they read gamma instead, an in-bounds, L2-resident stand-in whose
+  // values are never used.
+  const char* stand_in = static_cast<const char*>(p.gamma);
+  auto issue = [&](RowBuf<VPT, DRES>& b, int row) {
+    const bool live = row < r1;   // block-uniform
+    const int64_t off = static_cast<int64_t>(row) * h * EB;
+    const char* dyp = live ? static_cast<const char*>(p.dy) + off : stand_in;
+    const char* zp = live ? static_cast<const char*>(p.z) + off : stand_in;
+    const char* drp = DRES && live ? static_cast<const char*>(p.dres) + off : stand_in;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      b.dy[k] = ld16_stream(dyp + vv[k] * 16);
+      b.z[k] = ld16_stream(zp + vv[k] * 16);
+      if constexpr (DRES) b.dr[k] = ld16_stream(drp + vv[k] * 16);
+    }
+    const int srow = live ? row : r1 - 1;
+    b.mu = ln ? p.mean[srow] : 0.0f;
+    b.rs = p.rstd[srow];
+  };
+
   int parity = 0;
-  for (int64_t r = r0; r < r1; r += RPI) {
-    u32x4 rdy[RPI][VPT], rz[RPI][VPT], rdr[RPI][VPT];
-    float mu[RPI], rs[RPI];
+  auto process = [&](const RowBuf<VPT, DRES>& b, int row) {
+    if (row >= r1) return;   // block-uniform: every thread skips the barrier alike
+    const float mu = b.mu;
+    const float rs = b.rs;
+    float part[2] = {0.0f, 0.0f};
 #pragma unroll
-    for (int q = 0; q < RPI; ++q) {
-      const int64_t row = (r + q < r1) ? r + q : r1 - 1;   // clamped: loads stay in bounds
-      const int64_t off = row * static_cast<int64_t>(h) * EB;
+    for (int k = 0; k < VPT; ++k) {
+      if (!valid[k]) continue;
+      float zv[V], dyv[V];
+      unpack(E{}, b.z[k], zv);
+      unpack(E{}, b.dy[k], dyv);
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        rdy[q][k] = ld16_stream(static_cast<const char*>(p.dy) + off + vv[k] * 16);
-        rz[q][k] = ld16_stream(static_cast<const char*>(p.z) + off + vv[k] * 16);
-        if (p.dres) rdr[q][k] = ld16_stream(static_cast<const char*>(p.dres) + off + vv[k] * 16);
-      }
-      mu[q] = ln ? p.mean[row] : 0.0f;
-      rs[q] = p.rstd[row];
-    }
-
-    float xh[RPI][VPT][V], gg[RPI][VPT][V], dyv[RPI][VPT][V];
-    float sums[NR];
-#pragma unroll
-    for (int q = 0; q < RPI; ++q) {
-      sums[2 * q] = 0.0f;
-      sums[2 * q + 1] = 0.0f;
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        float zv[V];
-        unpack(E{}, rz[q][k], zv);
-        unpack(E{}, rdy[q][k], dyv[q][k]);
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-          xh[q][k][e] = (zv[e] - mu[q]) * rs[q];
-          gg[q][k][e] = dyv[q][k][e] * gam[k][e];
-        }
-        if (valid[k]) {
-#pragma unroll
-          for (int e = 0; e < V; ++e) {
-            sums[2 * q] += gg[q][k][e];
-            sums[2 * q + 1] = __builtin_fmaf(gg[q][k][e], xh[q][k][e], sums[2 * q + 1]);
-          }
-        }
+      for (int e = 0; e < V; ++e) {
+        const float xh = (zv[e] - mu) * rs;
+        const float gg = dyv[e] * gam[k][e];
+        part[0] += gg;
+        part[1] = __builtin_fmaf(gg, xh, part[1]);
       }
     }
-    block_sum<NR>(sums, red[parity]);
+    // One barrier per row; the two LDS slots alternate, so a slot is only
+    // rewritten after every wave has passed the barrier of the row between.
+    float* slot = red[parity];
     parity ^= 1;
-
+    wave_sum<2>(part);
+    if (lane == 0) {
+      slot[wave] = part[0];
+      slot[16 + wave] = part[1];
+    }
+    __syncthreads();
+    float s1 = slot[0], s2 = slot[16];
+    for (int w = 1; w < nwaves; ++w) {   // wave order: the same total in every thread
+      s1 += slot[w];
+      s2 += slot[16 + w];
+    }
+    const float c1 = ln ? s1 * inv_h : 0.0f;
+    const float c2 = s2 * inv_h;
+    const int64_t off = static_cast<int64_t>(row) * h * EB;
 #pragma unroll
-    for (int q = 0; q < RPI; ++q) {
-      if (r + q >= r1) break;
-      const int64_t off = (r + q) * static_cast<int64_t>(h) * EB;
-      const float c1 = ln ? sums[2 * q] * inv_h : 0.0f;
-      const float c2 = sums[2 * q + 1] * inv_h;
+    for (int k = 0; k < VPT; ++k) {
+      if (!valid[k]) continue;
+      float zv[V], dyv[V], dx[V];
+      unpack(E{}, b.z[k], zv);
+      unpack(E{}, b.dy[k], dyv);
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        if (!valid[k]) continue;
-        float dx[V];
-#pragma unroll
-        for (int e = 0; e < V; ++e) dx[e] = rs[q] * __builtin_fmaf(-xh[q][k][e], c2, gg[q][k][e] - c1);
-        if (p.dres) {
-          float f[V];
-          unpack(E{}, rdr[q][k], f);
-#pragma unroll
-          for (int e = 0; e < V; ++e) dx[e] += f[e];
-        }
-        st16(static_cast<char*>(p.dx) + off + vv[k] * 16, pack(E{}, dx));
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-          dg[k][e] = __builtin_fmaf(dyv[q][k][e], xh[q][k][e], dg[k][e]);
-          db[k][e] += dyv[q][k][e];
-        }
+      for (int e = 0; e < V; ++e) {
+        const float xh = (zv[e] - mu) * rs;
+        const float gg = dyv[e] * gam[k][e];
+        dx[e] = rs * __builtin_fmaf(-xh, c2, gg - c1);
+        dg[k][e] = __builtin_fmaf(dyv[e], xh, dg[k][e]);
+        db[k][e] += dyv[e];
       }
+      if constexpr (DRES) {
+        float f[V];
+        unpack(E{}, b.dr[k], f);
+#pragma unroll
+        for (int e = 0; e < V; ++e) dx[e] += f[e];
+      }
+      st16(static_cast<char*>(p.dx) + off + vv[k] * 16, pack(E{}, dx));
+    }
+  };
+
+  RowBuf<VPT, DRES> ring[RING];
+#pragma unroll
+  for (int j = 0; j < RING; ++j) issue(ring[j], r0 + j);
+  for (int r = r0; r < r1; r += RING) {
+#pragma unroll
+    for (int j = 0; j < RING; ++j) {
+      process(ring[j], r + j);
+      issue(ring[j], r + j + RING);
     }
   }
 
@@ -142,6 +176,7 @@ __global__ __launch_bounds__(MAXBS) void sp_region_bwd_rows_kernel(const BwdPara
 // 256 threads = 16 column quads x 16 groups of partials.
 constexpr int kColQuads = 16;
 constexpr int kGroups = 16;
+static_assert(kBwdMaxBlocks % kGroups == 0, "groups must split the partials evenly");
 
 __global__ __launch_bounds__(256) void sp_region_bwd_cols_kernel(const float* __restrict__ ws, int G, int h,
                                                                  float* __restrict__ dgamma,
@@ -153,12 +188,24 @@ __global__ __launch_bounds__(256) void sp_region_bwd_cols_kernel(const float* __
   const int c4 = blockIdx.x * kColQuads + cq;
   float4 sg = make_float4(0.f, 0.f, 0.f, 0.f), sb = sg;
   if (c4 < nq) {
+    // At most kBwdMaxBlocks / kGroups partials per group: all loads in flight
+    // together, then summed in ascending block order.
+    constexpr int kPer = kBwdMaxBlocks / kGroups;
     const int g0 = grp * G / kGroups, g1 = (grp + 1) * G / kGroups;
-    for (int g = g0; g < g1; ++g) {
-      const float4 a = reinterpret_cast<const float4*>(ws + static_cast<int64_t>(g) * 2 * h)[c4];
-      const float4 b = reinterpret_cast<const float4*>(ws + static_cast<int64_t>(g) * 2 * h + h)[c4];
-      sg.x += a.x; sg.y += a.y; sg.z += a.z; sg.w += a.w;
-      sb.x += b.x; sb.y += b.y; sb.z += b.z; sb.w += b.w;
+    float4 a[kPer], b[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (g0 + i < g1) {
+        a[i] = reinterpret_cast<const float4*>(ws + static_cast<int64_t>(g0 + i) * 2 * h)[c4];
+        b[i] = reinterpret_cast<const float4*>(ws + static_cast<int64_t>(g0 + i) * 2 * h + h)[c4];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (g0 + i < g1) {
+        sg.x += a[i].x; sg.y += a[i].y; sg.z += a[i].z; sg.w += a[i].w;
+        sb.x += b[i].x; sb.y += b[i].y; sb.z += b[i].z; sb.w += b[i].w;
+      }
     }
   }
   part[0][grp][cq] = sg;
@@ -176,30 +223,47 @@ __global__ __launch_bounds__(256) void sp_region_bwd_cols_kernel(const float* __
   }
 }
 
-// VPT = 1 keeps two rows in flight per block; VPT = 2 (h above 8192 bf16 /
-// 4096 f32) processes one row at a time to stay within 128 VGPRs at 1024
-// threads.
+#ifndef SPR_BWD_MAX_THREADS
+#define SPR_BWD_MAX_THREADS 512   // block size cap of the row stage
+#endif
+#ifndef SPR_BWD_RING
+#define SPR_BWD_RING 4            // rows in flight per block
+#endif
+
+// Ring depth per vectors-per-thread, so the packed ring fits the VGPRs the
+// block size leaves (wider rows keep fewer rows in flight).
+template <int VPT, int MAXBS>
+constexpr int ring_for() {
+  return VPT == 1 ? SPR_BWD_RING : (VPT == 2 && MAXBS <= 512 ? SPR_BWD_RING : (VPT == 2 ? 2 : 1));
+}
+
 template <class E>
 hipError_t launch_rows(const BwdParams& p, const Shape& sh, hipStream_t stream) {
-  constexpr int MAXBS = 1024;
+  constexpr int MAXBS = SPR_BWD_MAX_THREADS;
   const dim3 grid(static_cast<unsigned>(p.G)), block(sh.threads);
+  const bool dres = p.dres != nullptr;
+#define SPR_ROWS(VPT, DRES) \
+  hipLaunchKernelGGL((sp_region_bwd_rows_kernel<E, VPT, ring_for<VPT, MAXBS>(), DRES, MAXBS>), grid, block, 0, stream, p)
   switch (sh.vpt) {
-    case 1: hipLaunchKernelGGL((sp_region_bwd_rows_kernel<E, 1, 2, MAXBS>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((sp_region_bwd_rows_kernel<E, 2, 1, MAXBS>), grid, block, 0, stream, p); break;
+    case 1: if (dres) SPR_ROWS(1, true); else SPR_ROWS(1, false); break;
+    case 2: if (dres) SPR_ROWS(2, true); else SPR_ROWS(2, false); break;
+    case 4: if (dres) SPR_ROWS(4, true); else SPR_ROWS(4, false); break;
     default: return hipErrorInvalidValue;
   }
+#undef SPR_ROWS
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Smallest VPT in {1, 2} giving at most 1024 threads (h = 8192 bf16 -> 1 x 1024).
+// Smallest VPT in {1, 2, 4} within SPR_BWD_MAX_THREADS threads
+// (h = 8192 bf16 -> 2 x 512 at the default cap of 512).
 Shape bwd_shape(int h, int dtype) {
   const int vec = dtype == 1 ? 8 : 4;
   const int nvec = h / vec;
-  for (int vpt : {1, 2}) {
+  for (int vpt : {1, 2, 4}) {
     const int need = (nvec + vpt - 1) / vpt;
-    if (need <= 1024) return Shape{vpt, ((need + 63) / 64) * 64};
+    if (need <= SPR_BWD_MAX_THREADS) return Shape{vpt, ((need + 63) / 64) * 64};
   }
   return Shape{0, 0};
 }

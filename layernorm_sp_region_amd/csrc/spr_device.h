@@ -100,18 +100,50 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
 }
 
 // ---------------------------------------------------------------------------
-// Reductions.  The xor butterfly leaves bit-identical totals in every lane
-// (each step adds the same two values in both partner lanes), and the
+// Reductions.  Wave sums use DPP row steps plus readlane (below), and the
 // cross-wave stage sums the per-wave totals in wave order, so a block's
 // result is deterministic and uniform across its threads.
 // ---------------------------------------------------------------------------
+// DPP row operations of GFX9 (operand permutations inside each row of 16
+// lanes, applied by the VALU itself: no LDS round trip).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each row of 16 lanes: after the two quad steps every lane holds
+// its quad's sum, after the half mirror its 8-lane group's, after the mirror
+// its row's.  Each step adds the same two values in both partner lanes, so
+// all lanes of a row hold bit-identical totals.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  x += dpp<kDppRowMirror>(x);
+  return x;
+}
+
+// Wave total, uniform (scalar) and deterministic: the four row sums are
+// combined in row order.
+__device__ __forceinline__ float wave_total(float x) {
+  x = row16_sum(x);
+  const int xi = __builtin_bit_cast(int, x);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
 template <int N>
 __device__ __forceinline__ void wave_sum(float (&v)[N]) {
 #pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += __shfl_xor(v[i], off, kWave);
-  }
+  for (int i = 0; i < N; ++i) v[i] = wave_total(v[i]);
 }
 
 // Block-wide sum of N values per thread (blocks of at most 16 waves).  `slot`

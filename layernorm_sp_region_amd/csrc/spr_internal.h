@@ -53,7 +53,10 @@ struct BwdParams {
 // Number of row blocks of the backward's first stage (and of workspace
 // partials): a pure function of (T, h) so the workspace size is known
 // without a device query.  256 = one block per MI355X compute unit.
-constexpr int kBwdMaxBlocks = 256;
+#ifndef SPR_BWD_BLOCKS
+#define SPR_BWD_BLOCKS 256
+#endif
+constexpr int kBwdMaxBlocks = SPR_BWD_BLOCKS;
 inline int64_t bwd_blocks(int64_t T, int64_t /*h*/) { return T < kBwdMaxBlocks ? T : kBwdMaxBlocks; }
 
 // Launchers: return hipSuccess or the launch error.  `dtype` 0 = f32, 1 = bf16.
