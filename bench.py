@@ -12,6 +12,7 @@ Prints ONE JSON line on stdout; diagnostics go to stderr.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--sets R]
   python bench.py --summarize-rocprof DIR   # rocprofv3 output -> text summary
+  python bench.py --traffic FETCH_DIR WRITE_DIR   # --pmc runs -> HBM bytes per launch
 """
 from __future__ import annotations
 
@@ -250,6 +251,41 @@ def summarize_rocprof(d):
     print("\n".join(out))
 
 
+def _counter_means(d):
+    """{kernel-name prefix: mean counter value per dispatch} from a --pmc run."""
+    out = {}
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        acc = {}
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                acc.setdefault(r.get("Kernel_Name", ""), []).append(float(r.get("Counter_Value", 0)))
+        for k, v in acc.items():
+            out[k] = sum(v) / len(v)
+    return out
+
+
+def traffic_summary(fetch_dir, write_dir, copy_bytes=1 << 30):
+    """HBM traffic per launch of each region kernel from a FETCH_SIZE run and a
+    WRITE_SIZE run (KiB per dispatch), each scaled by what the same counter
+    reads for the calibration copy of known size."""
+    fe, wr = _counter_means(fetch_dir), _counter_means(write_dir)
+    pick = lambda m, key: next(v for k, v in m.items() if key in k)
+    f_scale = (copy_bytes / 1024) / pick(fe, "sp_region_copy_kernel")
+    w_scale = (copy_bytes / 1024) / pick(wr, "sp_region_copy_kernel")
+    lines = [f"# FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f} "
+             f"(1 GiB calibration copy: counter KiB vs true KiB)"]
+    fwd = None
+    for key in ("sp_region_fwd_kernel", "sp_region_bwd_rows_kernel", "sp_region_bwd_cols_kernel"):
+        fb = pick(fe, key) * f_scale * 1024
+        wb = pick(wr, key) * w_scale * 1024
+        lines.append(f"{key}: fetch_bytes={fb:.0f} write_bytes={wb:.0f} total_bytes={fb + wb:.0f}")
+        if key == "sp_region_fwd_kernel":
+            fwd = fb + wb
+    lines.append(f"kernel_source_sha256={kernel_source_hash()}")
+    lines.append(f"hbm_bytes_per_launch={fwd:.0f}")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -259,9 +295,13 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="rotating input/output sets (Infinity Cache defeat)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-rocprof", metavar="DIR")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof)
+        return
+    if args.traffic:
+        traffic_summary(*args.traffic)
         return
     if args.gpus != 1:
         eprint(f"bench.py measures one GPU's shard; --gpus {args.gpus} is not supported "

@@ -22,6 +22,16 @@
 namespace spr {
 namespace {
 
+#ifndef SPR_BWD_NT_STORE
+#define SPR_BWD_NT_STORE 1        // nontemporal stores for dx (measured: the next kernel no longer
+                                  // pays for writing back dirty dx lines)
+#endif
+
+__device__ __forceinline__ void st16_dx(void* p, u32x4 v) {
+  if constexpr (SPR_BWD_NT_STORE) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else st16(p, v);
+}
+
 // Packed loads of one row: VPT vectors of dy, z (and dres) per thread.
 // The row's statistics travel with its data: every lane loads the same
 // mean/rstd (one broadcast request per wave), so waiting for a ring slot
@@ -90,20 +100,24 @@ __global__ __launch_bounds__(MAXBS) void sp_region_bwd_rows_kernel(const BwdPara
     if (row >= r1) return;   // block-uniform: every thread skips the barrier alike
     const float mu = b.mu;
     const float rs = b.rs;
+    // xhat, g and dy of this row stay in registers between the two phases.
+    float xh[VPT][V], gg[VPT][V], dyv[VPT][V];
     float part[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      if (!valid[k]) continue;
-      float zv[V], dyv[V];
+      float zv[V];
       unpack(E{}, b.z[k], zv);
-      unpack(E{}, b.dy[k], dyv);
+      unpack(E{}, b.dy[k], dyv[k]);
+      float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        const float xh = (zv[e] - mu) * rs;
-        const float gg = dyv[e] * gam[k][e];
-        part[0] += gg;
-        part[1] = __builtin_fmaf(gg, xh, part[1]);
+        xh[k][e] = (zv[e] - mu) * rs;
+        gg[k][e] = dyv[k][e] * gam[k][e];
+        p0 += gg[k][e];
+        p1 = __builtin_fmaf(gg[k][e], xh[k][e], p1);
       }
+      part[0] += valid[k] ? p0 : 0.0f;
+      part[1] += valid[k] ? p1 : 0.0f;
     }
     // One barrier per row; the two LDS slots alternate, so a slot is only
     // rewritten after every wave has passed the barrier of the row between.
@@ -126,16 +140,12 @@ __global__ __launch_bounds__(MAXBS) void sp_region_bwd_rows_kernel(const BwdPara
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       if (!valid[k]) continue;
-      float zv[V], dyv[V], dx[V];
-      unpack(E{}, b.z[k], zv);
-      unpack(E{}, b.dy[k], dyv);
+      float dx[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        const float xh = (zv[e] - mu) * rs;
-        const float gg = dyv[e] * gam[k][e];
-        dx[e] = rs * __builtin_fmaf(-xh, c2, gg - c1);
-        dg[k][e] = __builtin_fmaf(dyv[e], xh, dg[k][e]);
-        db[k][e] += dyv[e];
+        dx[e] = rs * __builtin_fmaf(-xh[k][e], c2, gg[k][e] - c1);
+        dg[k][e] = __builtin_fmaf(dyv[k][e], xh[k][e], dg[k][e]);
+        db[k][e] += dyv[k][e];
       }
       if constexpr (DRES) {
         float f[V];
@@ -143,7 +153,7 @@ __global__ __launch_bounds__(MAXBS) void sp_region_bwd_rows_kernel(const BwdPara
 #pragma unroll
         for (int e = 0; e < V; ++e) dx[e] += f[e];
       }
-      st16(static_cast<char*>(p.dx) + off + vv[k] * 16, pack(E{}, dx));
+      st16_dx(static_cast<char*>(p.dx) + off + vv[k] * 16, pack(E{}, dx));
     }
   };
 

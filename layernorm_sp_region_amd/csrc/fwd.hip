@@ -31,15 +31,10 @@
 namespace spr {
 namespace {
 
-// Tuning knobs (defaults are the measured best on MI355X).
-#ifndef SPR_FWD_WAVES_PER_ROW
-#define SPR_FWD_WAVES_PER_ROW 1   // waves per row for rows of at least 512 vectors
-#endif
-#ifndef SPR_FWD_CHUNK
-#define SPR_FWD_CHUNK 1           // vectors per lane per streamed chunk
-#endif
-#ifndef SPR_FWD_NT_STORE
-#define SPR_FWD_NT_STORE 0        // nontemporal stores for z and y
+// Runtime loop over vector slots (1) or full unrolling (0) when z is in LDS;
+// measured: unrolled is ~1 us faster on a 2048 x 8192 shard.
+#ifndef SPR_FWD_LOOP
+#define SPR_FWD_LOOP 0
 #endif
 constexpr int kRowsPerBlockW1 = 4;   // WPR = 1: four independent rows per block
 
@@ -72,33 +67,35 @@ __device__ __forceinline__ float row_total(float x, float* slot) {
   }
 }
 
-// Loads of one chunk: C vectors x (NS slabs + residual) per lane.
-__device__ __forceinline__ void st16_out(void* p, u32x4 v) {
-  if constexpr (SPR_FWD_NT_STORE) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-  else st16(p, v);
-}
-
-template <int NS, int C>
-struct Chunk {
-  u32x4 s[C][NS];
-  u32x4 r[C];
-  u32x4 b[C];
+// Loads of one vector slot: the t slab vectors, the residual and the bias.
+template <int NS>
+struct Slot {
+  u32x4 s[NS];
+  u32x4 r;
+  u32x4 b;
 };
 
-// gamma/beta of the y phase are fetched kGB slots at a time, one group ahead.
-constexpr int kGB = 4;
-
-template <class E, int NS, int VPL, int C, int WPR>
-__global__ __launch_bounds__(WPR == 1 ? 64 * kRowsPerBlockW1 : 64 * WPR) void sp_region_fwd_kernel(const FwdParams p) {
+// At least 2 waves per SIMD: 8 rows per CU, which keeps a 2048-row shard
+// resident in one pass (the register budget caps how far loads are hoisted).
+template <class E, int NS, int VPL, int WPR, bool MASK>
+__global__ __launch_bounds__(WPR == 1 ? 64 * kRowsPerBlockW1 : 64 * WPR, 2) void sp_region_fwd_kernel(const FwdParams p) {
   constexpr int V = E::kVec;
   constexpr int EB = 16 / V;
-  constexpr int NCH = VPL / C;
-  static_assert(VPL % C == 0, "chunk must divide the vectors per lane");
   __shared__ float red[2][WPR];
+  // Packed z of the row lives in LDS when the row has 8-16 vectors per lane
+  // (each lane reads back only what it wrote, so no barrier is needed); that
+  // frees 32-64 VGPRs for the prefetch pipeline.  Short rows keep z in
+  // registers.
+  constexpr bool ZLDS = VPL <= 16 && VPL >= 8;
+  constexpr int ZW = WPR == 1 ? kRowsPerBlockW1 : WPR;
+  __shared__ u32x4 zlds[ZLDS ? ZW : 1][ZLDS ? VPL : 1][64];
 
   const int lane = threadIdx.x & 63;
-  const int wv = WPR == 1 ? 0 : threadIdx.x / 64;
-  const int64_t row = WPR == 1 ? static_cast<int64_t>(blockIdx.x) * kRowsPerBlockW1 + threadIdx.x / 64
+  // threadIdx.x / 64 is wave-uniform; readfirstlane tells the compiler, so the
+  // row's base pointers live in SGPRs.
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / 64));
+  const int wv = WPR == 1 ? 0 : wave;
+  const int64_t row = WPR == 1 ? static_cast<int64_t>(blockIdx.x) * kRowsPerBlockW1 + wave
                                : static_cast<int64_t>(blockIdx.x);
   if (row >= p.T) return;   // the whole wave (WPR = 1) or block (WPR > 1) leaves
 
@@ -107,181 +104,224 @@ __global__ __launch_bounds__(WPR == 1 ? 64 * kRowsPerBlockW1 : 64 * WPR) void sp
   const int64_t row_off = row * static_cast<int64_t>(h) * EB;   // bytes
   const int64_t slab_bytes = p.slab_stride * EB;
   const char* prow = static_cast<const char*>(p.partials) + row_off;
-  const char* rrow = static_cast<const char*>(p.residual) + row_off;
-  const bool has_res = p.residual != nullptr;
 
-  // Vector owned by slot k, clamped so that loads stay in bounds.
+  // Every memory instruction below is unconditional.  The waitcnt pass
+  // cannot count loads or stores issued under a branch, and would then wait
+  // for part of the prefetched slot before using the current one.  So:
+  //  * an absent residual / bias / beta is replaced by gamma, an in-bounds,
+  //    L2-resident stand-in whose values are never used (the branches that
+  //    apply them are arithmetic only);
+  //  * slots past the end of a row whose vector count is not a multiple of
+  //    64*WPR are clamped to the row's last vector: they recompute exactly
+  //    that vector's z, y and mask, so their stores write identical bytes.
+  const bool has_res = p.residual != nullptr;
+  const bool has_bias = p.bias != nullptr;
+  const bool has_beta = p.beta != nullptr;
+  const char* stand_in = static_cast<const char*>(p.gamma);
+  const char* rrow = has_res ? static_cast<const char*>(p.residual) + row_off : stand_in;
+  const char* biasp = has_bias ? static_cast<const char*>(p.bias) : stand_in;
+  const char* betap = has_beta ? static_cast<const char*>(p.beta) : stand_in;
+
   auto vec_of = [&](int k) {
     const int v = lane + 64 * (wv + WPR * k);
     return v < nvec ? v : nvec - 1;
   };
   auto valid = [&](int k) { return lane + 64 * (wv + WPR * k) < nvec; };
+  // Addresses are a wave-uniform base (SGPRs) plus a zero-extended 32-bit
+  // lane offset, the form global loads take as saddr + voffset.
+  auto lane_off = [&](int k) { return static_cast<uint32_t>(vec_of(k)) * 16u; };
 
-  const bool has_bias = p.bias != nullptr;
-  auto issue = [&](Chunk<NS, C>& ch, int c) {
+  auto issue = [&](Slot<NS>& sl, int k) {
+    const uint32_t o = lane_off(k);
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-      const int64_t o = static_cast<int64_t>(vec_of(c * C + i)) * 16;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) ch.s[i][s] = ld16_stream(prow + s * slab_bytes + o);
-      if (has_res) ch.r[i] = ld16_stream(rrow + o);
-      if (has_bias) ch.b[i] = ld16(static_cast<const char*>(p.bias) + o);
-    }
+    for (int s = 0; s < NS; ++s) sl.s[s] = ld16_stream(prow + s * slab_bytes + o);
+    sl.r = ld16_stream(rrow + o);
+    sl.b = ld16(biasp + o);
   };
 
   const uint64_t g = p.drop ? global_token(p, row) : 0;
   const uint32_t g_lo = static_cast<uint32_t>(g), g_hi = static_cast<uint32_t>(g >> 32);
 
-  u32x4 zs[VPL];   // rounded z, packed
-  float zsum = 0.0f;   // LayerNorm: sum of the rounded z, accumulated while streaming
-  Chunk<NS, C> buf[2];
-  issue(buf[0], 0);
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    if (c + 1 < NCH) issue(buf[(c + 1) & 1], c + 1);
-    Chunk<NS, C>& ch = buf[c & 1];
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-      const int k = c * C + i;
-      const int v = vec_of(k);
-      float acc[V];
-      unpack(E{}, ch.s[i][0], acc);
-#pragma unroll
-      for (int s = 1; s < NS; ++s) {
-        float f[V];
-        unpack(E{}, ch.s[i][s], f);
-#pragma unroll
-        for (int e = 0; e < V; ++e) acc[e] = acc[e] + f[e];
-      }
-      if (has_bias) {
-        float f[V];
-        unpack(E{}, ch.b[i], f);
-#pragma unroll
-        for (int e = 0; e < V; ++e) acc[e] = acc[e] + f[e];
-      }
-      uint8_t keep[V];
-#pragma unroll
-      for (int e = 0; e < V; ++e) keep[e] = 1;
-      if (p.drop) {
-#pragma unroll
-        for (int b4 = 0; b4 < V / 4; ++b4) {
-          const uint32_t blk = static_cast<uint32_t>(v * (V / 4) + b4);   // channel / 4
-          const Philox4 r = philox4x32_10(blk, g_lo, g_hi, 0u, p.key0, p.key1);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) keep[b4 * 4 + w] = r.w[w] >= p.thr;
-        }
-#pragma unroll
-        for (int e = 0; e < V; ++e) acc[e] = keep[e] ? acc[e] * p.scale : 0.0f;
-      }
-      if (has_res) {
-        float f[V];
-        unpack(E{}, ch.r[i], f);
-#pragma unroll
-        for (int e = 0; e < V; ++e) acc[e] = f[e] + acc[e];
-      }
-      zs[k] = pack(E{}, acc);
-      if (valid(k)) {
-        if (p.norm == 0) {
-          float f[V];
-          rounded_values(E{}, zs[k], f);
-#pragma unroll
-          for (int e = 0; e < V; ++e) zsum += f[e];
-        }
-        st16_out(static_cast<char*>(p.z) + row_off + v * 16, zs[k]);
-        if (p.mask) {
-          uint8_t* m = p.mask + row * static_cast<int64_t>(h) + v * V;
-          if constexpr (V == 8) {
-            uint2 mv;
-            mv.x = keep[0] | (keep[1] << 8) | (keep[2] << 16) | (keep[3] << 24);
-            mv.y = keep[4] | (keep[5] << 8) | (keep[6] << 16) | (keep[7] << 24);
-            *reinterpret_cast<uint2*>(m) = mv;
-          } else {
-            *reinterpret_cast<uint32_t*>(m) = keep[0] | (keep[1] << 8) | (keep[2] << 16) | (keep[3] << 24);
-          }
-        }
-      }
-    }
-  }
-
-  // gamma/beta of the first kGB slots: in flight during the statistics.
-  u32x4 gb[2][kGB][2];
-  auto issue_gb = [&](int grp) {
-#pragma unroll
-    for (int j = 0; j < kGB; ++j) {
-      const int k = grp * kGB + j;
-      if (k < VPL) {
-        const int64_t o = static_cast<int64_t>(vec_of(k)) * 16;
-        gb[grp & 1][j][0] = ld16(static_cast<const char*>(p.gamma) + o);
-        if (p.beta) gb[grp & 1][j][1] = ld16(static_cast<const char*>(p.beta) + o);
-      }
-    }
+  u32x4 zs[ZLDS ? 1 : VPL];   // rounded z, packed (when not in LDS)
+  auto zput = [&](int k, u32x4 v) {
+    if constexpr (ZLDS) zlds[wave][k][lane] = v;
+    else zs[k] = v;
   };
-  issue_gb(0);
+  auto zget = [&](int k) -> u32x4 {
+    if constexpr (ZLDS) return zlds[wave][k][lane];
+    else return zs[k];
+  };
 
-  // ---- statistics over the full h (from the rounded z) --------------------
-  const float inv_h = 1.0f / static_cast<float>(h);
-  float mean = 0.0f, q = 0.0f;
-  if (p.norm == 0) {
-    mean = row_total<WPR>(zsum, red[0]) * inv_h;
+  // z of slot k = round(residual + dropout(sum_s P_s + bias)); stores z (and
+  // the mask), returns this lane's sum of the rounded values (LayerNorm mean).
+  auto process = [&](const Slot<NS>& sl, int k) -> float {
+    const int v = vec_of(k);
+    float acc[V];
+    unpack(E{}, sl.s[0], acc);
 #pragma unroll
-    for (int k = 0; k < VPL; ++k)
-      if (valid(k)) {
-        float f[V];
-        rounded_values(E{}, zs[k], f);
+    for (int s = 1; s < NS; ++s) {
+      float f[V];
+      unpack(E{}, sl.s[s], f);
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const float d = f[e] - mean;
-          q = __builtin_fmaf(d, d, q);
-        }
+      for (int e = 0; e < V; ++e) acc[e] = acc[e] + f[e];
+    }
+    if (has_bias) {
+      float f[V];
+      unpack(E{}, sl.b, f);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = acc[e] + f[e];
+    }
+    uint8_t keep[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) keep[e] = 1;
+    if (p.drop) {
+#pragma unroll
+      for (int b4 = 0; b4 < V / 4; ++b4) {
+        const uint32_t blk = static_cast<uint32_t>(v * (V / 4) + b4);   // channel / 4
+        const Philox4 r = philox4x32_10(blk, g_lo, g_hi, 0u, p.key0, p.key1);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) keep[b4 * 4 + w] = r.w[w] >= p.thr;
       }
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = keep[e] ? acc[e] * p.scale : 0.0f;
+    }
+    if (has_res) {
+      float f[V];
+      unpack(E{}, sl.r, f);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = f[e] + acc[e];
+    }
+    const u32x4 zk = pack(E{}, acc);
+    zput(k, zk);
+    st16(static_cast<char*>(p.z) + row_off + lane_off(k), zk);
+    if constexpr (MASK) {
+      uint8_t* m = p.mask + row * static_cast<int64_t>(h) + static_cast<uint32_t>(v) * V;
+      if constexpr (V == 8) {
+        uint2 mv;
+        mv.x = keep[0] | (keep[1] << 8) | (keep[2] << 16) | (keep[3] << 24);
+        mv.y = keep[4] | (keep[5] << 8) | (keep[6] << 16) | (keep[7] << 24);
+        *reinterpret_cast<uint2*>(m) = mv;
+      } else {
+        *reinterpret_cast<uint32_t*>(m) = keep[0] | (keep[1] << 8) | (keep[2] << 16) | (keep[3] << 24);
+      }
+    }
+    float f[V];
+    rounded_values(E{}, zk, f);
+    float part = 0.0f;
+#pragma unroll
+    for (int e = 0; e < V; ++e) part += f[e];
+    return valid(k) ? part : 0.0f;
+  };
+
+  // ---- stream the row: slot k+1's loads are in flight while k is summed ----
+  constexpr bool LOOP = ZLDS && SPR_FWD_LOOP;
+  float zsum = 0.0f;
+  Slot<NS> A, B;
+  issue(A, 0);
+  if constexpr (LOOP) {
+    // Runtime loop over slot pairs; the last pair is peeled so that every
+    // iteration issues the same loads (VPL is even here).
+#pragma unroll 1
+    for (int k = 0; k < VPL - 2; k += 2) {
+      issue(B, k + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      zsum += process(A, k);
+      issue(A, k + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      zsum += process(B, k + 1);
+    }
+    issue(B, VPL - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    zsum += process(A, VPL - 2);
+    __builtin_amdgcn_sched_barrier(0);
+    zsum += process(B, VPL - 1);
   } else {
 #pragma unroll
-    for (int k = 0; k < VPL; ++k)
-      if (valid(k)) {
-        float f[V];
-        rounded_values(E{}, zs[k], f);
+    for (int k = 0; k < VPL; ++k) {
+      if (k + 1 < VPL) issue((k & 1) ? A : B, k + 1);   // compile-time after unrolling
+      __builtin_amdgcn_sched_barrier(0);
+      zsum += process((k & 1) ? B : A, k);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- statistics over the full h (from the rounded z) --------------------
+  // gamma/beta of slot 0 are in flight during the statistics.
+  auto issue_gb = [&](u32x4 (&gb)[2], int k) {
+    const uint32_t o = lane_off(k);
+    gb[0] = ld16(static_cast<const char*>(p.gamma) + o);
+    gb[1] = ld16(betap + o);
+  };
+  u32x4 GA[2], GB[2];
+  issue_gb(GA, 0);
+
+  const float inv_h = 1.0f / static_cast<float>(h);
+  const bool ln = p.norm == 0;
+  const float mean = ln ? row_total<WPR>(zsum, red[0]) * inv_h : 0.0f;
+  float q = 0.0f;
+#pragma unroll 2
+  for (int k = 0; k < VPL; ++k) {
+    float f[V];
+    rounded_values(E{}, zget(k), f);
+    float part = 0.0f;
 #pragma unroll
-        for (int e = 0; e < V; ++e) q = __builtin_fmaf(f[e], f[e], q);
-      }
+    for (int e = 0; e < V; ++e) {
+      const float d = f[e] - mean;   // mean = 0 for RMSNorm: the mean square
+      part = __builtin_fmaf(d, d, part);
+    }
+    q += valid(k) ? part : 0.0f;
   }
   const float rstd = 1.0f / __builtin_sqrtf(row_total<WPR>(q, red[1]) * inv_h + p.eps);
+
+  // ---- y = (z - mean)*rstd*gamma + beta, gamma/beta one slot ahead ---------
+  auto emit_y = [&](const u32x4 (&gb)[2], int k) {
+    float zf[V], gm[V], bt[V], yv[V];
+    rounded_values(E{}, zget(k), zf);
+    unpack(E{}, gb[0], gm);
+    unpack(E{}, gb[1], bt);
+    if (!has_beta) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) bt[e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) yv[e] = __builtin_fmaf((zf[e] - mean) * rstd, gm[e], bt[e]);
+    st16(static_cast<char*>(p.y) + row_off + lane_off(k), pack(E{}, yv));
+  };
+  if constexpr (LOOP) {
+#pragma unroll 1
+    for (int k = 0; k < VPL - 2; k += 2) {
+      issue_gb(GB, k + 1);
+      emit_y(GA, k);
+      issue_gb(GA, k + 2);
+      emit_y(GB, k + 1);
+    }
+    issue_gb(GB, VPL - 1);
+    emit_y(GA, VPL - 2);
+    emit_y(GB, VPL - 1);
+  } else {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      if (k + 1 < VPL) issue_gb((k & 1) ? GA : GB, k + 1);   // compile-time after unrolling
+      emit_y((k & 1) ? GB : GA, k);
+    }
+  }
   if (threadIdx.x % (64 * WPR) == 0) {
     if (p.mean) p.mean[row] = mean;
     p.rstd[row] = rstd;
-  }
-
-  // ---- y -------------------------------------------------------------------
-  constexpr int NG = (VPL + kGB - 1) / kGB;
-#pragma unroll
-  for (int grp = 0; grp < NG; ++grp) {
-    if (grp + 1 < NG) issue_gb(grp + 1);
-#pragma unroll
-    for (int j = 0; j < kGB; ++j) {
-      const int k = grp * kGB + j;
-      if (k >= VPL || !valid(k)) continue;
-      float zf[V], gm[V], bt[V], yv[V];
-      rounded_values(E{}, zs[k], zf);
-      unpack(E{}, gb[grp & 1][j][0], gm);
-      if (p.beta) unpack(E{}, gb[grp & 1][j][1], bt);
-      else {
-#pragma unroll
-        for (int e = 0; e < V; ++e) bt[e] = 0.0f;
-      }
-#pragma unroll
-      for (int e = 0; e < V; ++e) yv[e] = __builtin_fmaf((zf[e] - mean) * rstd, gm[e], bt[e]);
-      st16_out(static_cast<char*>(p.y) + row_off + vec_of(k) * 16, pack(E{}, yv));
-    }
   }
 }
 
 template <class E, int VPL, int WPR>
 hipError_t launch_ns(const FwdParams& p, hipStream_t stream) {
-  constexpr int C = VPL % SPR_FWD_CHUNK == 0 ? SPR_FWD_CHUNK : 1;
   const dim3 grid(static_cast<unsigned>(WPR == 1 ? (p.T + kRowsPerBlockW1 - 1) / kRowsPerBlockW1 : p.T));
   const dim3 block(WPR == 1 ? 64 * kRowsPerBlockW1 : 64 * WPR);
+  const bool mask = p.mask != nullptr;
   switch (p.t) {
-#define SPR_NS(N) \
-  case N: hipLaunchKernelGGL((sp_region_fwd_kernel<E, N, VPL, C, WPR>), grid, block, 0, stream, p); break;
+#define SPR_NS(N)                                                                                          \
+  case N:                                                                                                  \
+    if (mask) hipLaunchKernelGGL((sp_region_fwd_kernel<E, N, VPL, WPR, true>), grid, block, 0, stream, p); \
+    else hipLaunchKernelGGL((sp_region_fwd_kernel<E, N, VPL, WPR, false>), grid, block, 0, stream, p);     \
+    break;
     SPR_NS(1) SPR_NS(2) SPR_NS(3) SPR_NS(4) SPR_NS(5) SPR_NS(6) SPR_NS(7) SPR_NS(8)
 #undef SPR_NS
     default: return hipErrorInvalidValue;
@@ -291,50 +331,33 @@ hipError_t launch_ns(const FwdParams& p, hipStream_t stream) {
 
 template <class E>
 hipError_t launch_e(const FwdParams& p, const Shape& sh, hipStream_t stream) {
-  constexpr int W2 = SPR_FWD_WAVES_PER_ROW;
   if (sh.threads == 64) {
     switch (sh.vpt) {
       case 1: return launch_ns<E, 1, 1>(p, stream);
       case 2: return launch_ns<E, 2, 1>(p, stream);
       case 4: return launch_ns<E, 4, 1>(p, stream);
       case 8: return launch_ns<E, 8, 1>(p, stream);
-      default:
-        if constexpr (W2 == 1) {
-          if (sh.vpt == 16) return launch_ns<E, 16, 1>(p, stream);
-          if (sh.vpt == 32) return launch_ns<E, 32, 1>(p, stream);
-        }
-        return hipErrorInvalidValue;
+      case 16: return launch_ns<E, 16, 1>(p, stream);
+      default: return hipErrorInvalidValue;
     }
   }
-  if constexpr (W2 > 1) {
-    switch (sh.vpt) {
-      case 4: return launch_ns<E, 4, W2>(p, stream);
-      case 8: return launch_ns<E, 8, W2>(p, stream);
-      case 16: return launch_ns<E, 16, W2>(p, stream);
-      default: break;
-    }
-  }
+  if (sh.threads == 128 && sh.vpt == 16) return launch_ns<E, 16, 2>(p, stream);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// Waves per row and vectors per lane.  Rows of fewer than 512 vectors get one
-// wave (threads = 64) and the smallest power-of-two VPL covering them; longer
-// rows get SPR_FWD_WAVES_PER_ROW waves (threads = 64*WPR).
-// (h = 8192 bf16 -> 2 waves x 8; h = 5120 -> 2 x 8 with 3 slots predicated off;
-//  h = 512 f32 -> 1 x 2.)
+// Waves per row and vectors per lane: rows of up to 1024 vectors (h <= 8192
+// bf16, 4096 f32) get one wave and the smallest power-of-two VPL covering
+// them; wider rows (up to 2048 vectors) get two waves of 16.  Shape.threads
+// is 64 * waves per row.  (h = 8192 bf16 -> 1 x 16; h = 5120 -> 1 x 16 with
+// 6 slots clamped; h = 512 f32 -> 1 x 2; h = 16384 bf16 -> 2 x 16.)
 Shape fwd_shape(int h, int dtype) {
   const int vec = dtype == 1 ? 8 : 4;
   const int nvec = h / vec;
-  constexpr int W2 = SPR_FWD_WAVES_PER_ROW;
-  if (nvec < 512 || W2 == 1) {
-    for (int vpl : {1, 2, 4, 8, 16, 32})
-      if (nvec <= 64 * vpl) return Shape{vpl, 64};
-    return Shape{0, 0};
-  }
-  for (int vpl : {4, 8, 16})
-    if (nvec <= 64 * W2 * vpl) return Shape{vpl, 64 * W2};
+  for (int vpl : {1, 2, 4, 8, 16})
+    if (nvec <= 64 * vpl) return Shape{vpl, 64};
+  if (nvec <= 2 * 64 * 16) return Shape{16, 128};
   return Shape{0, 0};
 }
 
