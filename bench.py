@@ -127,8 +127,15 @@ def run(args):
     dt = gamma.dtype
     sets = []
     base = dict(P=tt(inp["partials"]), res=tt(inp["residual"]), dy=tt(inp["dy"]))
+    # Slab layout: the library's recommended stride (the receive-buffer layout
+    # a caller controls) unless --slabs contiguous (stride T*h).
+    stride = spr.partials_stride(T, h, dt) if args.slabs == "recommended" and T * h > 0 else T * h
     for i in range(args.sets):
         s = {k: (v if i == 0 or v is None else v.clone()) for k, v in base.items()}
+        if args.slabs == "recommended":
+            P = spr.empty_partials(w.t, T, h, dt, dev)
+            P.copy_(s["P"])
+            s["P"] = P
         ln = w.norm == "layernorm"
         s["fo"] = spr.FwdOut(torch.empty((T, h), dtype=dt, device=dev), torch.empty((T, h), dtype=dt, device=dev),
                              torch.empty(T, device=dev) if ln else None, torch.empty(T, device=dev), None)
@@ -174,13 +181,25 @@ def run(args):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Timed region: exactly K steps, nothing else on the stream.  (A timing
+    # event costs the GPU a few microseconds at every record, so the per-launch
+    # events go in the second, otherwise identical, pass below.)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+
+    # Kernel durations: the same K steps with events around every launch, on
+    # the stream the library launches on (torch's current stream).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed_ev = time.perf_counter() - t1
 
     fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
@@ -189,7 +208,8 @@ def run(args):
     achieved = fb / fwd_s / 1e9
     step_ms = elapsed / args.steps * 1e3
     eprint(f"[bench] fwd {fwd_ms.mean() * 1e3:.1f} us (p50 {np.median(fwd_ms) * 1e3:.1f}), "
-           f"bwd {bwd_ms.mean() * 1e3:.1f} us, step {step_ms * 1e3:.1f} us wall; fwd {achieved:.0f} GB/s, "
+           f"bwd {bwd_ms.mean() * 1e3:.1f} us, step {step_ms * 1e3:.1f} us wall "
+           f"({elapsed_ev / args.steps * 1e6:.1f} with events); fwd {achieved:.0f} GB/s, "
            f"fwd+bwd {(fb + bb) / ((fwd_ms.mean() + bwd_ms.mean()) * 1e-3) / 1e9:.0f} GB/s")
 
     traffic = read_traffic()
@@ -209,7 +229,9 @@ def run(args):
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1)/sqrt(8) partial slabs, N(0,1) residual and dy, shaped like the pages' workloads)",
         "config": {"workload": w.name, "s": inp["s"], "b": inp["b"], "h": h, "t": w.t, "local_tokens": T,
-                   "p_drop": w.p_drop, "norm": w.norm, "rank": 0, "rotating_sets": args.sets},
+                   "p_drop": w.p_drop, "norm": w.norm, "rank": 0, "rotating_sets": args.sets,
+                   "slabs": args.slabs, "slab_stride": stride},
+        "step_us_with_events": elapsed_ev / args.steps * 1e6,
         "fwd_us": float(fwd_ms.mean() * 1e3),
         "bwd_us": float(bwd_ms.mean() * 1e3),
         "fwd_bwd_hbm_gbs": (fb + bb) / (kernel_us * 1e-6) / 1e9,
@@ -293,6 +315,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="shard70b")
     ap.add_argument("--sets", type=int, default=4, help="rotating input/output sets (Infinity Cache defeat)")
+    ap.add_argument("--slabs", choices=("recommended", "contiguous"), default="recommended",
+                    help="partial-slab layout: sp_region_partials_stride, or back to back (stride T*h)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-rocprof", metavar="DIR")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -305,7 +329,7 @@ def main():
         return
     if args.gpus != 1:
         eprint(f"bench.py measures one GPU's shard; --gpus {args.gpus} is not supported "
-               "(this build runs on a single MI355X: no collectives, no multi-GPU launch)")
+               "(the region runs on one MI355X: no collectives or multi-GPU launch are implemented)")
         sys.exit(2)
     run(args)
 

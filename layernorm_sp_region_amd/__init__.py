@@ -36,6 +36,7 @@ SIGNATURES = {
     "sp_region_last_hip_error": (ctypes.c_int, []),
     "sp_region_fwd": (ctypes.c_int, [_I64, _I64, _I64, _I32, _F32, _F32, _VP, _VP, _I32, _I32, _I32, _U64,
                                      _VP, _I64, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "sp_region_partials_stride": (_I64, [_I64, _I64, _I32]),
     "sp_region_bwd_workspace_bytes": (_SZ, [_I64, _I64]),
     "sp_region_bwd": (ctypes.c_int, [_I64, _I64, _I64, _I32, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
                                      _VP, _VP, _VP, _VP, _SZ, _VP]),
@@ -193,6 +194,20 @@ def fwd(partials, gamma, beta=None, *, bias=None, residual=None, b: int, s: int,
                            _ptr(mask), stream)
     _check("sp_region_fwd", st)
     return FwdOut(z, y, mean, rstd, mask)
+
+
+def partials_stride(T: int, h: int, dtype) -> int:
+    """Recommended element stride between the t partial slabs (see
+    sp_region_partials_stride in include/sp_region.h)."""
+    return int(load_library().sp_region_partials_stride(T, h, _dtype_code(dtype)))
+
+
+def empty_partials(t: int, T: int, h: int, dtype, device):
+    """Uninitialised [t][T][h] slabs laid out with the recommended stride."""
+    import torch
+    stride = partials_stride(T, h, dtype) if T * h > 0 else T * h
+    buf = torch.empty(t * stride, dtype=dtype, device=device)
+    return buf.as_strided((t, T, h), (stride, h, 1))
 
 
 def workspace_bytes(T: int, h: int) -> int:

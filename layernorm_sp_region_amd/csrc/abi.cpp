@@ -117,6 +117,13 @@ int sp_region_fwd(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p
   return hip_status(spr::launch_fwd(p, dtype, static_cast<hipStream_t>(stream)));
 }
 
+int64_t sp_region_partials_stride(int64_t n_local_tokens, int64_t h, int32_t dtype) {
+  if (n_local_tokens <= 0 || h <= 0 || (dtype != SPR_F32 && dtype != SPR_BF16)) return 0;
+  const int64_t eb = dtype == SPR_BF16 ? 2 : 4;
+  const int64_t bytes = n_local_tokens * h * eb;
+  return ((bytes + 2047) / 2048 * 2048 + 1024) / eb;
+}
+
 size_t sp_region_bwd_workspace_bytes(int64_t n_local_tokens, int64_t h) {
   if (n_local_tokens <= 0 || h <= 0) return 0;
   return static_cast<size_t>(spr::bwd_blocks(n_local_tokens, h)) * 2u * static_cast<size_t>(h) * sizeof(float);

@@ -14,8 +14,9 @@
 // block); each row's two sums take one block reduction.
 //
 // Stage 2 (sp_region_bwd_cols_kernel): dgamma/dbeta = the G partials summed in
-// ascending block order, split over 16 groups whose sums are combined in
+// ascending block order, split over 32 groups whose sums are combined in
 // group order -- a fixed tree, so results are bitwise reproducible.
+
 #include "spr_device.h"
 #include "spr_internal.h"
 
@@ -32,6 +33,14 @@ __device__ __forceinline__ void st16_dx(void* p, u32x4 v) {
   else st16(p, v);
 }
 
+#ifndef SPR_WS_NT
+#define SPR_WS_NT 0
+#endif
+__device__ __forceinline__ void st16_ws(void* p, u32x4 v) {
+  if constexpr (SPR_WS_NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else st16(p, v);
+}
+
 // Packed loads of one row: VPT vectors of dy, z (and dres) per thread.
 // The row's statistics travel with its data: every lane loads the same
 // mean/rstd (one broadcast request per wave), so waiting for a ring slot
@@ -42,8 +51,10 @@ struct RowBuf {
   float mu, rs;
 };
 
-template <class E, int VPT, int RING, bool DRES, int MAXBS>
-__global__ __launch_bounds__(MAXBS) void sp_region_bwd_rows_kernel(const BwdParams p) {
+// Stage 1 for block blockIdx.x: dx of its rows, and its [2][h] partial of
+// dgamma/dbeta in the workspace.
+template <class E, int VPT, int RING, bool DRES>
+__device__ __forceinline__ void rows_stage(const BwdParams& p) {
   constexpr int V = E::kVec;
   constexpr int EB = 16 / V;
   __shared__ float red[2][2 * 16];
@@ -175,62 +186,90 @@ __global__ __launch_bounds__(MAXBS) void sp_region_bwd_rows_kernel(const BwdPara
     if (!valid[k]) continue;
 #pragma unroll
     for (int e0 = 0; e0 < V; e0 += 4) {
-      st16(wsg + vv[k] * V + e0, u32x4{__float_as_uint(dg[k][e0]), __float_as_uint(dg[k][e0 + 1]),
-                                       __float_as_uint(dg[k][e0 + 2]), __float_as_uint(dg[k][e0 + 3])});
-      st16(wsb + vv[k] * V + e0, u32x4{__float_as_uint(db[k][e0]), __float_as_uint(db[k][e0 + 1]),
-                                       __float_as_uint(db[k][e0 + 2]), __float_as_uint(db[k][e0 + 3])});
+      st16_ws(wsg + vv[k] * V + e0, u32x4{__float_as_uint(dg[k][e0]), __float_as_uint(dg[k][e0 + 1]),
+                                          __float_as_uint(dg[k][e0 + 2]), __float_as_uint(dg[k][e0 + 3])});
+      st16_ws(wsb + vv[k] * V + e0, u32x4{__float_as_uint(db[k][e0]), __float_as_uint(db[k][e0 + 1]),
+                                          __float_as_uint(db[k][e0 + 2]), __float_as_uint(db[k][e0 + 3])});
     }
   }
 }
 
-// 256 threads = 16 column quads x 16 groups of partials.
-constexpr int kColQuads = 16;
-constexpr int kGroups = 16;
+template <class E, int VPT, int RING, bool DRES, int MAXBS>
+__global__ __launch_bounds__(MAXBS) void sp_region_bwd_rows_kernel(const BwdParams p) {
+  rows_stage<E, VPT, RING, DRES>(p);
+}
+
+// Stage 2: the G partials of each column are summed in a fixed tree: 32
+// groups of consecutive partials, each summed in ascending block order, then
+// the 32 group sums in group order.  The tree depends only on G.
+#ifndef SPR_BWD_GROUPS
+#define SPR_BWD_GROUPS 32   // 16 and 64 measured slower (latency-bound loads / half-line segments)
+#endif
+constexpr int kGroups = SPR_BWD_GROUPS;
 static_assert(kBwdMaxBlocks % kGroups == 0, "groups must split the partials evenly");
 
-__global__ __launch_bounds__(256) void sp_region_bwd_cols_kernel(const float* __restrict__ ws, int G, int h,
-                                                                 float* __restrict__ dgamma,
-                                                                 float* __restrict__ dbeta) {
-  __shared__ float4 part[2][kGroups][kColQuads];
-  const int cq = threadIdx.x % kColQuads;
-  const int grp = threadIdx.x / kColQuads;
+// Column quads [q0, q1) of dgamma/dbeta, cw = blockDim.x / kGroups quads at
+// a time (cw <= CQMAX); thread (group, quad) = (threadIdx.x / cw, threadIdx.x %
+// cw).  Every thread of the block calls this (it has barriers).
+template <int CQMAX>
+__device__ __forceinline__ void reduce_cols(const float* __restrict__ ws, int G, int h, int q0, int q1,
+                                            float* __restrict__ dgamma, float* __restrict__ dbeta) {
+  __shared__ float4 part[2][kGroups][CQMAX];
+  const int cw = static_cast<int>(blockDim.x) / kGroups;
+  const int cq = threadIdx.x % cw;
+  const int grp = threadIdx.x / cw;   // < kGroups since blockDim.x = kGroups * cw
+  // At most kBwdMaxBlocks / kGroups partials per group: all loads in flight
+  // together, then summed in ascending block order.
+  constexpr int kPer = kBwdMaxBlocks / kGroups;
+  const int g0 = grp * G / kGroups, g1 = (grp + 1) * G / kGroups;
+  for (int qb = q0; qb < q1; qb += cw) {   // block-uniform
+    const int c4 = qb + cq;
+    float4 sg = make_float4(0.f, 0.f, 0.f, 0.f), sb = sg;
+    if (c4 < q1) {
+      float4 a[kPer], b[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        if (g0 + i < g1) {
+          a[i] = reinterpret_cast<const float4*>(ws + static_cast<int64_t>(g0 + i) * 2 * h)[c4];
+          b[i] = reinterpret_cast<const float4*>(ws + static_cast<int64_t>(g0 + i) * 2 * h + h)[c4];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        if (g0 + i < g1) {
+          sg.x += a[i].x; sg.y += a[i].y; sg.z += a[i].z; sg.w += a[i].w;
+          sb.x += b[i].x; sb.y += b[i].y; sb.z += b[i].z; sb.w += b[i].w;
+        }
+      }
+    }
+    part[0][grp][cq] = sg;
+    part[1][grp][cq] = sb;
+    __syncthreads();
+    if (grp == 0 && c4 < q1) {
+      float4 tg = part[0][0][cq], tb = part[1][0][cq];
+      for (int i = 1; i < kGroups; ++i) {
+        const float4 a = part[0][i][cq], b = part[1][i][cq];
+        tg.x += a.x; tg.y += a.y; tg.z += a.z; tg.w += a.w;
+        tb.x += b.x; tb.y += b.y; tb.z += b.z; tb.w += b.w;
+      }
+      reinterpret_cast<float4*>(dgamma)[c4] = tg;
+      if (dbeta) reinterpret_cast<float4*>(dbeta)[c4] = tb;
+    }
+    __syncthreads();   // part is rewritten by the next chunk
+  }
+}
+
+#ifndef SPR_COLS_QPB
+#define SPR_COLS_QPB 8    // column quads per block of stage 2: 128-byte segments of each partial
+#endif
+constexpr int kColQuads = SPR_COLS_QPB;
+
+__global__ __launch_bounds__(kColQuads * kGroups) void sp_region_bwd_cols_kernel(const float* __restrict__ ws, int G,
+                                                                                 int h, float* __restrict__ dgamma,
+                                                                                 float* __restrict__ dbeta) {
   const int nq = h / 4;
-  const int c4 = blockIdx.x * kColQuads + cq;
-  float4 sg = make_float4(0.f, 0.f, 0.f, 0.f), sb = sg;
-  if (c4 < nq) {
-    // At most kBwdMaxBlocks / kGroups partials per group: all loads in flight
-    // together, then summed in ascending block order.
-    constexpr int kPer = kBwdMaxBlocks / kGroups;
-    const int g0 = grp * G / kGroups, g1 = (grp + 1) * G / kGroups;
-    float4 a[kPer], b[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      if (g0 + i < g1) {
-        a[i] = reinterpret_cast<const float4*>(ws + static_cast<int64_t>(g0 + i) * 2 * h)[c4];
-        b[i] = reinterpret_cast<const float4*>(ws + static_cast<int64_t>(g0 + i) * 2 * h + h)[c4];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      if (g0 + i < g1) {
-        sg.x += a[i].x; sg.y += a[i].y; sg.z += a[i].z; sg.w += a[i].w;
-        sb.x += b[i].x; sb.y += b[i].y; sb.z += b[i].z; sb.w += b[i].w;
-      }
-    }
-  }
-  part[0][grp][cq] = sg;
-  part[1][grp][cq] = sb;
-  __syncthreads();
-  if (grp == 0 && c4 < nq) {
-    float4 tg = part[0][0][cq], tb = part[1][0][cq];
-    for (int i = 1; i < kGroups; ++i) {
-      const float4 a = part[0][i][cq], b = part[1][i][cq];
-      tg.x += a.x; tg.y += a.y; tg.z += a.z; tg.w += a.w;
-      tb.x += b.x; tb.y += b.y; tb.z += b.z; tb.w += b.w;
-    }
-    reinterpret_cast<float4*>(dgamma)[c4] = tg;
-    if (dbeta) reinterpret_cast<float4*>(dbeta)[c4] = tb;
-  }
+  const int q0 = blockIdx.x * kColQuads;
+  reduce_cols<kColQuads>(ws, G, h, q0, q0 + kColQuads < nq ? q0 + kColQuads : nq, dgamma, dbeta);
 }
 
 #ifndef SPR_BWD_MAX_THREADS
@@ -247,21 +286,29 @@ constexpr int ring_for() {
   return VPT == 1 ? SPR_BWD_RING : (VPT == 2 && MAXBS <= 512 ? SPR_BWD_RING : (VPT == 2 ? 2 : 1));
 }
 
+template <class E, int VPT, bool DRES>
+hipError_t launch_stages(const BwdParams& p, const Shape& sh, hipStream_t stream) {
+  constexpr int MAXBS = SPR_BWD_MAX_THREADS;
+  constexpr int RING = ring_for<VPT, MAXBS>();
+  const dim3 grid(static_cast<unsigned>(p.G)), block(sh.threads);
+  hipLaunchKernelGGL((sp_region_bwd_rows_kernel<E, VPT, RING, DRES, MAXBS>), grid, block, 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nq = p.h / 4;
+  hipLaunchKernelGGL(sp_region_bwd_cols_kernel, dim3((nq + kColQuads - 1) / kColQuads), dim3(kColQuads * kGroups), 0,
+                     stream, p.ws, p.G, p.h, p.dgamma, p.dbeta);
+  return hipGetLastError();
+}
+
 template <class E>
 hipError_t launch_rows(const BwdParams& p, const Shape& sh, hipStream_t stream) {
-  constexpr int MAXBS = SPR_BWD_MAX_THREADS;
-  const dim3 grid(static_cast<unsigned>(p.G)), block(sh.threads);
   const bool dres = p.dres != nullptr;
-#define SPR_ROWS(VPT, DRES) \
-  hipLaunchKernelGGL((sp_region_bwd_rows_kernel<E, VPT, ring_for<VPT, MAXBS>(), DRES, MAXBS>), grid, block, 0, stream, p)
   switch (sh.vpt) {
-    case 1: if (dres) SPR_ROWS(1, true); else SPR_ROWS(1, false); break;
-    case 2: if (dres) SPR_ROWS(2, true); else SPR_ROWS(2, false); break;
-    case 4: if (dres) SPR_ROWS(4, true); else SPR_ROWS(4, false); break;
+    case 1: return dres ? launch_stages<E, 1, true>(p, sh, stream) : launch_stages<E, 1, false>(p, sh, stream);
+    case 2: return dres ? launch_stages<E, 2, true>(p, sh, stream) : launch_stages<E, 2, false>(p, sh, stream);
+    case 4: return dres ? launch_stages<E, 4, true>(p, sh, stream) : launch_stages<E, 4, false>(p, sh, stream);
     default: return hipErrorInvalidValue;
   }
-#undef SPR_ROWS
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -281,12 +328,12 @@ Shape bwd_shape(int h, int dtype) {
 hipError_t launch_bwd(const BwdParams& p, int dtype, hipStream_t stream) {
   if (p.G > 0) {
     const Shape sh = bwd_shape(p.h, dtype);
-    const hipError_t e = dtype == 1 ? launch_rows<Bf16>(p, sh, stream) : launch_rows<F32>(p, sh, stream);
-    if (e != hipSuccess) return e;
+    return dtype == 1 ? launch_rows<Bf16>(p, sh, stream) : launch_rows<F32>(p, sh, stream);
   }
+  // No rows: dgamma = dbeta = 0 (every group is empty).
   const int nq = p.h / 4;
-  const dim3 grid((nq + kColQuads - 1) / kColQuads), block(kColQuads * kGroups);
-  hipLaunchKernelGGL(sp_region_bwd_cols_kernel, grid, block, 0, stream, p.ws, p.G, p.h, p.dgamma, p.dbeta);
+  hipLaunchKernelGGL(sp_region_bwd_cols_kernel, dim3((nq + kColQuads - 1) / kColQuads), dim3(kColQuads * kGroups), 0,
+                     stream, p.ws, p.G, p.h, p.dgamma, p.dbeta);
   return hipGetLastError();
 }
 

@@ -51,6 +51,23 @@ def test_version_and_strerror(lib):
     assert lib.sp_region_last_hip_error() == 0
 
 
+def test_partials_stride_recommendation(lib):
+    ps = lib.sp_region_partials_stride
+    assert ps(0, 8192, 1) == 0 and ps(10, 0, 1) == 0 and ps(-3, 8, 0) == 0 and ps(10, 8, 7) == 0
+    assert ps(2048, 8192, 1) == 2048 * 8192 + 512      # 32 MiB slabs -> 1 KiB apart in residue
+    assert ps(2048, 8192, 0) == 2048 * 8192 + 256      # float32: the same 1 KiB
+    for T, h, dt in [(1, 8, 1), (3, 520, 1), (5, 4, 0), (2731, 5120, 1), (16384, 8192, 1), (7, 8192, 0)]:
+        eb = 2 if dt == 1 else 4
+        st = ps(T, h, dt)
+        assert st >= T * h
+        assert (st * eb) % 2048 == 1024                  # odd multiple of 1 KiB modulo 2 KiB
+        assert (st * eb) % 16 == 0                       # a stride the forward accepts
+        assert st * eb - T * h * eb < 3072               # the smallest such stride
+    import torch
+    assert spr.partials_stride(2048, 8192, torch.bfloat16) == ps(2048, 8192, 1)
+    assert spr.partials_stride(2048, 8192, torch.float32) == ps(2048, 8192, 0)
+
+
 def test_workspace_bytes_is_pure(lib):
     ws = lib.sp_region_bwd_workspace_bytes
     assert ws(0, 8192) == 0 and ws(10, 0) == 0 and ws(-1, 8) == 0

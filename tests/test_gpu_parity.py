@@ -45,11 +45,17 @@ def to_np_f64(x):
     return x.float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(inp, w, rank, device, dres=None, padded_slabs=0, return_mask=True):
+def run_gpu(inp, w, rank, device, dres=None, padded_slabs=0, return_mask=True, recommended_stride=False):
     import torch
     t = lambda a: W.as_torch(a, device)
     P = inp["partials"]
-    if padded_slabs:
+    if recommended_stride:
+        Pc = t(P)
+        Pt = spr.empty_partials(P.shape[0], P.shape[1], P.shape[2], Pc.dtype, device)
+        Pt.copy_(Pc)
+        assert Pt.stride(0) == spr.partials_stride(P.shape[1], P.shape[2], Pc.dtype) > P.shape[1] * P.shape[2]
+        del Pc
+    elif padded_slabs:
         Pp = np.zeros((P.shape[0], P.shape[1] + padded_slabs, P.shape[2]), dtype=P.dtype)
         Pp[:, :P.shape[1]] = P
         Pt = t(Pp)[:, :P.shape[1], :]
@@ -127,13 +133,17 @@ def inputs_for(w):
     return _INPUTS[w.name]
 
 
-@pytest.mark.parametrize("name,rank", [("tiny", 0), ("tiny", 3), ("page_demo", 0), ("page_demo", 7),
-                                       ("shard70b", 0), ("shard70b", 7), ("ragged13b", 0), ("ragged13b", 7)])
-def test_workload_parity(cuda_device, name, rank):
+# Each workload at the first and last rank; the slabs contiguous or at the
+# recommended stride (the layout the benchmark times).
+@pytest.mark.parametrize("name,rank,layout", [("tiny", 0, "contiguous"), ("tiny", 3, "recommended"),
+                                              ("page_demo", 0, "recommended"), ("page_demo", 7, "contiguous"),
+                                              ("shard70b", 0, "recommended"), ("shard70b", 7, "contiguous"),
+                                              ("ragged13b", 0, "recommended"), ("ragged13b", 7, "contiguous")])
+def test_workload_parity(cuda_device, name, rank, layout):
     w = W.BY_NAME[name]
-    log(f"[parity] {name} rank={rank}")
+    log(f"[parity] {name} rank={rank} slabs={layout}")
     inp = inputs_for(w)
-    gpu = run_gpu(inp, w, rank, cuda_device)
+    gpu = run_gpu(inp, w, rank, cuda_device, recommended_stride=layout == "recommended")
     compare(w, inp, gpu, rank)
 
 
