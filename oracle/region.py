@@ -4,7 +4,9 @@ What it computes, on one rank's shard of T = b*s/t rows by h channels:
 
   forward   z = residual + dropout(sum_k P_k + bias)        (one rank's g* output)
             y = LayerNorm(z) or RMSNorm(z)                   (per token, over all h)
-  backward  dx = d(loss)/dz (+ an optional extra gradient on z), dgamma, dbeta
+  backward  dx = d(loss)/dz (+ an optional extra gradient on z), dgamma, dbeta;
+            through the dropout: dpartial = d(loss)/dP_k (the same for every
+            slab k) and dbias
 
 Sources (hpc.payai.win, lesson 7 "Sequence parallelism"):
   * section 2 gives LayerNorm over the full hidden size: mean and population
@@ -84,9 +86,12 @@ def normalize(z64: np.ndarray, gamma64: np.ndarray, beta64: Optional[np.ndarray]
 
 
 def encode(x32: np.ndarray, dtype: str) -> np.ndarray:
-    """float32 values -> storage array (bf16 bits rounded to nearest even)."""
+    """float32 values -> storage array (bf16 bits rounded to nearest even);
+    "f64" keeps float64 values."""
     if dtype == "bf16":
         return f32_to_bf16(x32)
+    if dtype == "f64":
+        return np.asarray(x32, dtype=np.float64)
     return np.asarray(x32, dtype=np.float32)
 
 
@@ -142,7 +147,10 @@ def region_forward(partials, *, t, rank, dtype, norm, eps, p_drop, seed,
                    rows=None, chunk=256):
     """Forward of the region on one rank's shard.
 
-    partials: [t][T][h] storage array (float32, or uint16 bf16 bits).
+    partials: [t][T][h] storage array (float32, or uint16 bf16 bits; float64
+              values with dtype "f64", which runs the whole pre-norm sum in
+              float64 with no rounding -- the mode the finite-difference
+              pins of the backward differentiate).
     rows:     optional local row indices to evaluate (default all rows).
     Returns dict with z (storage), z32 (its float32 value), keep (bool),
     y, mean (None for RMSNorm), rstd -- y/mean/rstd in float64.
@@ -158,8 +166,9 @@ def region_forward(partials, *, t, rank, dtype, norm, eps, p_drop, seed,
     scale = dropout_scale(p_drop)
     eps64 = float(np.float32(eps))
 
-    z_out = np.empty((n, h), dtype=np.float32 if dtype == "f32" else np.uint16)
-    z32_out = np.empty((n, h), dtype=np.float32)
+    acc_t = np.float64 if dtype == "f64" else np.float32   # arithmetic of the pre-norm sum
+    z_out = np.empty((n, h), dtype={"f32": np.float32, "f64": np.float64}.get(dtype, np.uint16))
+    z32_out = np.empty((n, h), dtype=acc_t)
     keep_out = np.empty((n, h), dtype=bool)
     y = np.empty((n, h), dtype=np.float64)
     mean = np.empty(n, dtype=np.float64) if norm == LAYERNORM else None
@@ -169,16 +178,16 @@ def region_forward(partials, *, t, rank, dtype, norm, eps, p_drop, seed,
         r = rows[a:a + chunk]
         acc = decode(partials[0][r], dtype).copy()                   # g*: sum of the t slabs
         for k in range(1, t):
-            acc = (acc + decode(partials[k][r], dtype)).astype(np.float32)
+            acc = (acc + decode(partials[k][r], dtype)).astype(acc_t)
         if bias32 is not None:
-            acc = (acc + bias32[None, :]).astype(np.float32)
+            acc = (acc + bias32[None, :]).astype(acc_t)
         keep = keep_mask(seed, p_drop, gidx_all[r], h)
         if p_drop > 0.0:
-            d = np.where(keep, (acc * scale).astype(np.float32), np.float32(0.0)).astype(np.float32)
+            d = np.where(keep, (acc * scale).astype(acc_t), acc_t(0.0)).astype(acc_t)
         else:
             d = acc
         if residual is not None:
-            zf = (decode(residual[r], dtype) + d).astype(np.float32)
+            zf = (decode(residual[r], dtype) + d).astype(acc_t)
         else:
             zf = d
         zs = encode(zf, dtype)
@@ -194,6 +203,33 @@ def region_forward(partials, *, t, rank, dtype, norm, eps, p_drop, seed,
         y[a:a + len(r)] = yy
 
     return dict(z=z_out, z32=z32_out, keep=keep_out, y=y, mean=mean, rstd=rstd, rows=rows)
+
+
+def dropout_backward(dx, *, t, rank, p_drop, seed, cu_seqlens=None, T=None, rows=None):
+    """Gradient of the slab sum and of the bias, given dx = d(loss)/dz (float64).
+
+    The backward of each forward step is its adjoint (lesson 7, section 3.B):
+    z = residual + dropout(a) with a = sum_k P_k + bias, and inverted dropout
+    multiplies kept elements by scale = float32(1/(1-p)) and zeroes the rest,
+    so d(loss)/da = dx * keep * scale, with the forward's own mask (same
+    seed, same global token index).  The sum over the t slabs is linear with
+    coefficient 1 for every slab, so d(loss)/dP_k is that same tensor for
+    every k -- in the multi-GPU pipeline it is what the backward of g* (an
+    all-gather, section 3.B) delivers to each rank's row-linear.  The bias
+    gradient is its column sum over this rank's rows.
+
+    dx:   float64 [n][h] for local rows `rows` (default all T rows, T = n).
+    Returns dict: dpartial [n][h], dbias [h], C [h] = sum_i |dpartial_ij|
+    (the conditioning scale of dbias), keep [n][h].
+    """
+    n, h = dx.shape
+    T = n if T is None else T
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    assert len(rows) == n
+    keep = keep_mask(seed, p_drop, token_index(T, t, rank, cu_seqlens)[rows], h)
+    scale = float(dropout_scale(p_drop)) if p_drop > 0.0 else 1.0
+    dpartial = np.where(keep, dx * scale, 0.0)
+    return dict(dpartial=dpartial, dbias=dpartial.sum(axis=0), C=np.abs(dpartial).sum(axis=0), keep=keep)
 
 
 def region_backward(dy, z, gamma, *, dtype, norm, eps, dres_in=None, rows=None, chunk=256,

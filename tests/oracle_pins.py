@@ -315,3 +315,71 @@ def check_dbeta_is_column_sum(seed=11, T=64, h=32, R=R):
     out = R.region_backward(dy, z, gamma, dtype="f32", norm="layernorm", eps=1e-5)
     for j in range(h):
         assert abs(out["dbeta"][j] - math.fsum(float(v) for v in dy[:, j])) <= 1e-12 * out["B"][j]
+
+
+def check_dropout_backward_finite_differences(norm="layernorm", ragged=False, seed=12, T=3, h=8, t=2, rank=1,
+                                              p=0.4, R=R):
+    """Central differences in float64 through the whole region forward
+    (dtype "f64": no rounding anywhere), of L = sum(dy * y) + sum(dres * z),
+    with respect to one element of every slab, the bias and the residual,
+    against the oracle's dropout_backward(region_backward(...)).  The mask is
+    the forward's own; a ragged shard checks that both sides use the same
+    global token index (brute force)."""
+    rng = _rng(seed)
+    P = rng.standard_normal((t, T, h))
+    res = rng.standard_normal((T, h))
+    bias = 0.3 * rng.standard_normal(h)
+    gamma = rng.uniform(0.5, 1.5, h)
+    beta = rng.standard_normal(h) if norm == "layernorm" else None
+    dy = rng.standard_normal((T, h))
+    dres = rng.standard_normal((T, h))
+    cu = np.array([0, 1, T], dtype=np.int64) if ragged else None
+    eps, sd = 1e-3, 0x1234_5678_9ABC
+    kw = dict(t=t, rank=rank, dtype="f64", norm=norm, eps=eps, p_drop=p, seed=sd, gamma=gamma, beta=beta,
+              cu_seqlens=cu)
+
+    def L():
+        o = oracle_region.region_forward(P, bias=bias, residual=res, **kw)
+        return float(np.sum(dy * o["y"]) + np.sum(dres * o["z"]))
+
+    fwd = R.region_forward(P, bias=bias, residual=res, **kw)
+    assert 0 < (~fwd["keep"]).sum() < fwd["keep"].size        # some dropped, some kept
+    bw = R.region_backward(dy, fwd["z"], gamma, dtype="f64", norm=norm, eps=eps, dres_in=dres)
+    out = R.dropout_backward(bw["dx"], t=t, rank=rank, p_drop=p, seed=sd, cu_seqlens=cu)
+    d = 1e-6
+
+    def fd(arr, idx):
+        a0 = arr[idx]
+        arr[idx] = a0 + d
+        lp = L()
+        arr[idx] = a0 - d
+        lm = L()
+        arr[idx] = a0
+        return (lp - lm) / (2 * d)
+
+    for k in (0, t - 1):
+        dp_fd = np.array([[fd(P, (k, i, j)) for j in range(h)] for i in range(T)])
+        assert np.max(np.abs(out["dpartial"] - dp_fd)) < 1e-6 * max(1.0, np.max(np.abs(dp_fd))), f"slab {k}"
+    db_fd = np.array([fd(bias, j) for j in range(h)])
+    assert np.max(np.abs(out["dbias"] - db_fd)) < 1e-6 * max(1.0, np.max(np.abs(db_fd))), "dbias"
+    dr_fd = np.array([[fd(res, (i, j)) for j in range(h)] for i in range(T)])
+    assert np.max(np.abs(bw["dx"] - dr_fd)) < 1e-6 * max(1.0, np.max(np.abs(dr_fd))), "dresidual"
+
+
+def check_dropout_backward_special_cases(seed=13, T=20, h=24, t=4, rank=2, R=R):
+    """p = 0 leaves the gradient unchanged (no mask, no scale); with p > 0 the
+    zero pattern of dpartial is the forward's dropped set and dbias is the
+    exact column sum (math.fsum) of dpartial."""
+    rng = _rng(seed)
+    dx = rng.standard_normal((T, h))
+    out0 = R.dropout_backward(dx, t=t, rank=rank, p_drop=0.0, seed=5)
+    assert np.array_equal(out0["dpartial"], dx)
+    P = rng.standard_normal((t, T, h)).astype(np.float32)
+    gamma = np.ones(h, dtype=np.float32)
+    fwd = oracle_region.region_forward(P, t=t, rank=rank, dtype="f32", norm="rmsnorm", eps=1e-5, p_drop=0.35,
+                                       seed=77, gamma=gamma)
+    out = R.dropout_backward(dx, t=t, rank=rank, p_drop=0.35, seed=77)
+    assert np.array_equal(out["dpartial"] != 0.0, fwd["keep"])
+    for j in range(h):
+        assert out["dbias"][j] == math.fsum(out["dpartial"][:, j]) or \
+            abs(out["dbias"][j] - math.fsum(out["dpartial"][:, j])) <= 1e-12 * out["C"][j]

@@ -36,8 +36,8 @@ REGION_MUTATIONS = [
      lambda R: pins.check_z_within_exact_bound(R=R)),
     ("no_residual", "zf = (decode(residual[r], dtype) + d)", "zf = (0 * decode(residual[r], dtype) + d)",
      lambda R: pins.check_z_within_exact_bound(R=R)),
-    ("round_each_add", "acc = (acc + decode(partials[k][r], dtype)).astype(np.float32)",
-     "acc = decode(encode((acc + decode(partials[k][r], dtype)).astype(np.float32), dtype), dtype)",
+    ("round_each_add", "acc = (acc + decode(partials[k][r], dtype)).astype(acc_t)",
+     "acc = decode(encode((acc + decode(partials[k][r], dtype)).astype(acc_t), dtype), dtype)",
      lambda R: pins.check_z_within_exact_bound(dtype="bf16", R=R)),
     ("unbiased_variance", "var = ((z64 - mu[..., None]) ** 2).mean(axis=-1)",
      "var = ((z64 - mu[..., None]) ** 2).sum(axis=-1) / (z64.shape[-1] - 1)",
@@ -69,6 +69,20 @@ REGION_MUTATIONS = [
      lambda R: pins.check_backward_finite_differences("rmsnorm", R=R)),
     ("bwd_dres_ignored", "d = d + decode(dres_in[r], dtype).astype(np.float64)", "d = d",
      lambda R: pins.check_backward_matches_torch_autograd("rmsnorm", R=R)),
+    ("dropout_bwd_no_scale", "dpartial = np.where(keep, dx * scale, 0.0)", "dpartial = np.where(keep, dx, 0.0)",
+     lambda R: pins.check_dropout_backward_finite_differences(R=R)),
+    ("dropout_bwd_mask_inverted", "dpartial = np.where(keep, dx * scale, 0.0)",
+     "dpartial = np.where(~keep, dx * scale, 0.0)",
+     lambda R: pins.check_dropout_backward_finite_differences(R=R)),
+    ("dropout_bwd_rank_ignored", "keep = keep_mask(seed, p_drop, token_index(T, t, rank, cu_seqlens)[rows], h)",
+     "keep = keep_mask(seed, p_drop, token_index(T, t, 0, cu_seqlens)[rows], h)",
+     lambda R: pins.check_dropout_backward_finite_differences(R=R)),
+    ("dropout_bwd_uniform_index", "keep = keep_mask(seed, p_drop, token_index(T, t, rank, cu_seqlens)[rows], h)",
+     "keep = keep_mask(seed, p_drop, token_index(T, t, rank, None)[rows], h)",
+     lambda R: pins.check_dropout_backward_finite_differences(ragged=True, R=R)),
+    ("dropout_bwd_dbias_from_dx", "return dict(dpartial=dpartial, dbias=dpartial.sum(axis=0),",
+     "return dict(dpartial=dpartial, dbias=dx.sum(axis=0),",
+     lambda R: pins.check_dropout_backward_finite_differences(R=R)),
 ]
 
 

@@ -21,3 +21,12 @@ def test_scale_identities(norm):
 
 def test_dbeta_is_column_sum():
     pins.check_dbeta_is_column_sum()
+
+
+@pytest.mark.parametrize("norm,ragged", [("layernorm", False), ("rmsnorm", False), ("layernorm", True)])
+def test_dropout_backward_finite_differences(norm, ragged):
+    pins.check_dropout_backward_finite_differences(norm, ragged)
+
+
+def test_dropout_backward_special_cases():
+    pins.check_dropout_backward_special_cases()
