@@ -55,6 +55,12 @@ def bwd_bytes(w, T):
     return 3 * T * h * E + T * 4 * nstat + h * E + h * 4 * nstat
 
 
+def bwd_dropout_bytes(w, T):
+    """The backward through the dropout: bwd_bytes plus dpartial written
+    (T*h) and dbias written (h float32)."""
+    return bwd_bytes(w, T) + T * w.h * w.elem_bytes + w.h * 4
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for p in FWD_KERNEL_SOURCES:
@@ -201,6 +207,26 @@ def run(args):
     torch.cuda.synchronize()
     elapsed_ev = time.perf_counter() - t1
 
+    # The backward through the dropout and the slab sum (dpartial, dbias), on
+    # the same forward outputs: events around each of K launches.
+    ws_d = torch.empty(max(16, spr.dropout_workspace_bytes(T, h)), dtype=torch.uint8, device=dev)
+    douts = []
+    for s in sets:
+        bo = s["bo"]
+        douts.append(spr.BwdDropoutOut(bo.dx, torch.empty_like(bo.dx), bo.dgamma, bo.dbeta,
+                                       torch.empty(h, device=dev) if w.has_bias else None))
+    evd = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        s, fo = sets[i % len(sets)], sets[i % len(sets)]["fo"]
+        evd[i][0].record()
+        spr.bwd_dropout(s["dy"], fo.z, fo.mean, fo.rstd, gamma, b=inp["b"], s=inp["s"], t=w.t, rank=0,
+                        p_drop=w.p_drop, seed=inp["seed"], norm=w.norm, cu_seqlens=cu, workspace=ws_d,
+                        want_dbias=w.has_bias, out=douts[i % len(sets)])
+        evd[i][1].record()
+    torch.cuda.synchronize()
+    bwd_dropout_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evd]) * 1e3)
+    del douts, ws_d
+
     fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     fb, bb = fwd_bytes(w, T), bwd_bytes(w, T)
@@ -236,7 +262,9 @@ def run(args):
         "bwd_us": float(bwd_ms.mean() * 1e3),
         "fwd_bwd_hbm_gbs": (fb + bb) / (kernel_us * 1e-6) / 1e9,
         "fwd_bwd_pct_of_peak": 100 * (fb + bb) / (kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-        "algorithmic_bytes": {"fwd": fb, "bwd": bb},
+        "algorithmic_bytes": {"fwd": fb, "bwd": bb, "bwd_dropout": bwd_dropout_bytes(w, T)},
+        "bwd_dropout_us": bwd_dropout_us,
+        "bwd_dropout_hbm_gbs": bwd_dropout_bytes(w, T) / (bwd_dropout_us * 1e-6) / 1e9,
         "copy_ceiling_gbs": copy_gbs,
         "roofline": {"kernel": "sp_region_fwd_kernel", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},

@@ -175,6 +175,49 @@ int sp_region_bwd(int64_t b, int64_t s, int64_t h, int32_t t,
                   void* stream);
 
 /*
+ * Bytes of device workspace sp_region_bwd_dropout needs for T rows of h
+ * channels: float32 [G][3][h] (dgamma, dbeta and dbias partials), G as for
+ * sp_region_bwd_workspace_bytes.  A pure function; 0 for T <= 0 or h <= 0.
+ */
+size_t sp_region_bwd_dropout_workspace_bytes(int64_t n_local_tokens, int64_t h);
+
+/*
+ * Backward of the whole region below the normalisation: everything
+ * sp_region_bwd computes, plus the gradients through the dropout and the g*
+ * sum (hpc.payai.win lesson 7 "Sequence parallelism", section 3.B: the
+ * backward of each step is its adjoint, and g*'s backward is an all-gather
+ * that hands every TP rank the same gradient of its row-linear output).
+ *
+ *   b, s, h, t, gamma, norm, dtype, dy, z, mean, rstd, dres_in, dx, dgamma,
+ *   dbeta        as in sp_region_bwd (dx includes dres_in).
+ *   p_drop, rank, seed, cu_seqlens, nseq
+ *                the forward's dropout arguments, with the same meaning and
+ *                checks as in sp_region_fwd: the mask is recomputed from them,
+ *                never stored.
+ *   dpartial     out [T][h], the gradient of the slab sum sum_k P_k (the same
+ *                for every slab k) and of the pre-dropout activation:
+ *                dx * keep * float32(1/(1-p_drop)), computed from the float32
+ *                dx before its rounding and rounded once; p_drop == 0 gives
+ *                dpartial = dx.  Required when T > 0.
+ *   dbias        out float32 [h] or NULL: sum of dpartial over the T rows, in
+ *                the same fixed order as dgamma/dbeta.
+ *   workspace    >= sp_region_bwd_dropout_workspace_bytes(T, h) bytes,
+ *                16-byte aligned.  Contents are scratch.
+ *
+ * Results are bitwise reproducible for a given (T, h); dx, dgamma and dbeta
+ * are bitwise those of sp_region_bwd on the same inputs.
+ */
+int sp_region_bwd_dropout(int64_t b, int64_t s, int64_t h, int32_t t,
+                          const void* gamma, int32_t norm, int32_t dtype,
+                          const void* dy, const void* z, const float* mean, const float* rstd,
+                          const void* dres_in,
+                          float p_drop, int32_t rank, uint64_t seed,
+                          const int32_t* cu_seqlens, int32_t nseq,
+                          void* dx, void* dpartial, float* dgamma, float* dbeta, float* dbias,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
  * Calibration kernel: copies nbytes (a multiple of 16) from src to dst with
  * 16-byte loads and stores, for measuring the achievable HBM copy rate and for
  * scaling hardware traffic counters.  Not part of the region's computation.

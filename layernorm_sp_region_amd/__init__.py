@@ -40,6 +40,10 @@ SIGNATURES = {
     "sp_region_bwd_workspace_bytes": (_SZ, [_I64, _I64]),
     "sp_region_bwd": (ctypes.c_int, [_I64, _I64, _I64, _I32, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
                                      _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "sp_region_bwd_dropout_workspace_bytes": (_SZ, [_I64, _I64]),
+    "sp_region_bwd_dropout": (ctypes.c_int, [_I64, _I64, _I64, _I32, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
+                                             _F32, _I32, _U64, _VP, _I32,
+                                             _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "sp_region_hbm_copy": (ctypes.c_int, [_VP, _VP, _SZ, _VP]),
 }
 
@@ -162,17 +166,7 @@ def fwd(partials, gamma, beta=None, *, bias=None, residual=None, b: int, s: int,
     _require(beta, "beta", dev, dt, (h,))
     _require(bias, "bias", dev, dt, (h,))
     _require(residual, "residual", dev, dt, (T, h))
-    nseq = 0
-    cu_dev = None
-    if cu_seqlens is not None:
-        if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
-            _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
-            cu_dev = cu_seqlens
-        else:
-            cu_list = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
-            check_cu_seqlens(cu_list, T)
-            cu_dev = torch.tensor(cu_list, dtype=torch.int32, device=dev)
-        nseq = cu_dev.numel() - 1
+    cu_dev, nseq = _cu_on_device(cu_seqlens, T, dev)
     ln = nc == SPR_LAYERNORM
     if out is None:
         z = torch.empty((T, h), dtype=dt, device=dev)
@@ -212,6 +206,22 @@ def empty_partials(t: int, T: int, h: int, dtype, device):
 
 def workspace_bytes(T: int, h: int) -> int:
     return int(load_library().sp_region_bwd_workspace_bytes(T, h))
+
+
+def _cu_on_device(cu_seqlens, T, dev):
+    """(device int32 offsets or None, nseq).  Host offsets are checked here
+    (the library cannot check a device array without a sync)."""
+    import torch
+    if cu_seqlens is None:
+        return None, 0
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
+        _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
+        cu_dev = cu_seqlens
+    else:
+        cu_list = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+        check_cu_seqlens(cu_list, T)
+        cu_dev = torch.tensor(cu_list, dtype=torch.int32, device=dev)
+    return cu_dev, cu_dev.numel() - 1
 
 
 def bwd(dy, z, mean, rstd, gamma, *, b: int, s: int, t: int, norm: Union[str, int] = "layernorm",
@@ -255,6 +265,64 @@ def bwd(dy, z, mean, rstd, gamma, *, b: int, s: int, t: int, norm: Union[str, in
                            workspace.numel(), stream)
     _check("sp_region_bwd", st)
     return BwdOut(dx, dgamma, dbeta)
+
+
+def dropout_workspace_bytes(T: int, h: int) -> int:
+    return int(load_library().sp_region_bwd_dropout_workspace_bytes(T, h))
+
+
+BwdDropoutOut = namedtuple("BwdDropoutOut", "dx dpartial dgamma dbeta dbias")
+
+
+def bwd_dropout(dy, z, mean, rstd, gamma, *, b: int, s: int, t: int, rank: int, p_drop: float, seed: int,
+                norm: Union[str, int] = "layernorm", cu_seqlens=None, dres_in=None, want_dbeta: bool = True,
+                want_dbias: bool = True, workspace=None, out: Optional["BwdDropoutOut"] = None) -> "BwdDropoutOut":
+    """Backward of the region through the dropout and the slab sum: BwdOut's
+    dx, dgamma, dbeta plus dpartial (the gradient of every slab) and dbias.
+    p_drop, rank, seed and cu_seqlens are the forward's."""
+    import torch
+    lib = load_library()
+    nc = _norm_code(norm)
+    dev = z.device
+    dt = z.dtype
+    dcode = _dtype_code(dt)
+    T, h = z.shape
+    if T != local_tokens(b, s, t):
+        raise ValueError(f"z holds {T} rows, expected b*s/t = {local_tokens(b, s, t)}")
+    ln = nc == SPR_LAYERNORM
+    _require(z, "z", dev, dt, (T, h))
+    _require(dy, "dy", dev, dt, (T, h))
+    _require(dres_in, "dres_in", dev, dt, (T, h))
+    _require(gamma, "gamma", dev, dt, (h,))
+    _require(mean, "mean", dev, torch.float32, (T,))
+    _require(rstd, "rstd", dev, torch.float32, (T,))
+    if ln and mean is None:
+        raise ValueError("LayerNorm backward needs mean")
+    cu_dev, nseq = _cu_on_device(cu_seqlens, T, dev)
+    need = dropout_workspace_bytes(T, h)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _require(workspace, "workspace", dev, torch.uint8)
+    if out is None:
+        dx = torch.empty((T, h), dtype=dt, device=dev)
+        dpartial = torch.empty((T, h), dtype=dt, device=dev)
+        dgamma = torch.empty((h,), dtype=torch.float32, device=dev)
+        dbeta = torch.empty((h,), dtype=torch.float32, device=dev) if (ln and want_dbeta) else None
+        dbias = torch.empty((h,), dtype=torch.float32, device=dev) if want_dbias else None
+    else:
+        dx, dpartial, dgamma, dbeta, dbias = out
+        _require(dx, "dx", dev, dt, (T, h))
+        _require(dpartial, "dpartial", dev, dt, (T, h))
+        _require(dgamma, "dgamma", dev, torch.float32, (h,))
+        _require(dbeta, "dbeta", dev, torch.float32, (h,))
+        _require(dbias, "dbias", dev, torch.float32, (h,))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.sp_region_bwd_dropout(b, s, h, t, _ptr(gamma), nc, dcode, _ptr(dy), _ptr(z),
+                                   _ptr(mean if ln else None), _ptr(rstd), _ptr(dres_in), float(p_drop), rank,
+                                   int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(cu_dev), nseq, _ptr(dx), _ptr(dpartial),
+                                   _ptr(dgamma), _ptr(dbeta), _ptr(dbias), _ptr(workspace), workspace.numel(), stream)
+    _check("sp_region_bwd_dropout", st)
+    return BwdDropoutOut(dx, dpartial, dgamma, dbeta, dbias)
 
 
 def hbm_copy(src, dst) -> None:

@@ -129,20 +129,28 @@ size_t sp_region_bwd_workspace_bytes(int64_t n_local_tokens, int64_t h) {
   return static_cast<size_t>(spr::bwd_blocks(n_local_tokens, h)) * 2u * static_cast<size_t>(h) * sizeof(float);
 }
 
-int sp_region_bwd(int64_t b, int64_t s, int64_t h, int32_t t,
-                  const void* gamma, int32_t norm, int32_t dtype,
-                  const void* dy, const void* z, const float* mean, const float* rstd,
-                  const void* dres_in,
-                  void* dx, float* dgamma, float* dbeta,
-                  void* workspace, size_t workspace_bytes,
-                  void* stream) {
+size_t sp_region_bwd_dropout_workspace_bytes(int64_t n_local_tokens, int64_t h) {
+  if (n_local_tokens <= 0 || h <= 0) return 0;
+  return static_cast<size_t>(spr::bwd_blocks(n_local_tokens, h)) * 3u * static_cast<size_t>(h) * sizeof(float);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both backward entry points; fills the normalisation part
+// of the parameters.
+int prepare_bwd(int64_t b, int64_t s, int64_t h, int32_t t, const void* gamma, int32_t norm, int32_t dtype,
+                const void* dy, const void* z, const float* mean, const float* rstd, const void* dres_in, void* dx,
+                float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes, bool with_dropout,
+                spr::BwdParams* p) {
   int64_t T = 0;
-  int st = check_shape(b, s, h, t, norm, dtype, &T);
+  const int st = check_shape(b, s, h, t, norm, dtype, &T);
   if (st != SPR_OK) return st;
+  const size_t need = with_dropout ? sp_region_bwd_dropout_workspace_bytes(T, h) : sp_region_bwd_workspace_bytes(T, h);
   const bool ln = norm == SPR_LAYERNORM;
   if (!gamma || !dgamma) return SPR_ERR_INVALID_ARG;
   if (!ln && dbeta != nullptr) return SPR_ERR_INVALID_ARG;
-  const size_t need = sp_region_bwd_workspace_bytes(T, h);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return SPR_ERR_INVALID_ARG;
   if (T > 0) {
     if (!dy || !z || !rstd || !dx) return SPR_ERR_INVALID_ARG;
@@ -152,22 +160,77 @@ int sp_region_bwd(int64_t b, int64_t s, int64_t h, int32_t t,
                           static_cast<const void*>(dx), static_cast<const void*>(dgamma),
                           static_cast<const void*>(dbeta), static_cast<const void*>(workspace)})
     if (!aligned16_or_null(ptr)) return SPR_ERR_ALIGNMENT;
+  *p = spr::BwdParams{};
+  p->dy = dy;
+  p->z = z;
+  p->mean = mean;
+  p->rstd = rstd;
+  p->gamma = gamma;
+  p->dres = dres_in;
+  p->dx = dx;
+  p->ws = static_cast<float*>(workspace);
+  p->dgamma = dgamma;
+  p->dbeta = dbeta;
+  p->T = T;
+  p->h = static_cast<int32_t>(h);
+  p->norm = norm;
+  p->G = static_cast<int32_t>(spr::bwd_blocks(T, h));
+  p->nparts = 1;
+  if (dbeta) p->slot_dbeta = p->nparts++;
+  return SPR_OK;
+}
 
-  spr::BwdParams p{};
-  p.dy = dy;
-  p.z = z;
-  p.mean = mean;
-  p.rstd = rstd;
-  p.gamma = gamma;
-  p.dres = dres_in;
-  p.dx = dx;
-  p.ws = static_cast<float*>(workspace);
-  p.dgamma = dgamma;
-  p.dbeta = dbeta;
-  p.T = T;
-  p.h = static_cast<int32_t>(h);
-  p.norm = norm;
-  p.G = static_cast<int32_t>(spr::bwd_blocks(T, h));
+}  // namespace
+
+extern "C" {
+
+int sp_region_bwd(int64_t b, int64_t s, int64_t h, int32_t t,
+                  const void* gamma, int32_t norm, int32_t dtype,
+                  const void* dy, const void* z, const float* mean, const float* rstd,
+                  const void* dres_in,
+                  void* dx, float* dgamma, float* dbeta,
+                  void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  spr::BwdParams p;
+  const int st = prepare_bwd(b, s, h, t, gamma, norm, dtype, dy, z, mean, rstd, dres_in, dx, dgamma, dbeta,
+                             workspace, workspace_bytes, false, &p);
+  if (st != SPR_OK) return st;
+  return hip_status(spr::launch_bwd(p, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int sp_region_bwd_dropout(int64_t b, int64_t s, int64_t h, int32_t t,
+                          const void* gamma, int32_t norm, int32_t dtype,
+                          const void* dy, const void* z, const float* mean, const float* rstd,
+                          const void* dres_in,
+                          float p_drop, int32_t rank, uint64_t seed,
+                          const int32_t* cu_seqlens, int32_t nseq,
+                          void* dx, void* dpartial, float* dgamma, float* dbeta, float* dbias,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  spr::BwdParams p;
+  const int st = prepare_bwd(b, s, h, t, gamma, norm, dtype, dy, z, mean, rstd, dres_in, dx, dgamma, dbeta,
+                             workspace, workspace_bytes, true, &p);
+  if (st != SPR_OK) return st;
+  if (!(p_drop >= 0.0f && p_drop < 1.0f)) return SPR_ERR_INVALID_ARG;
+  if (rank < 0 || rank >= t) return SPR_ERR_INVALID_ARG;
+  if (cu_seqlens != nullptr && (nseq < 1 || b != 1)) return SPR_ERR_INVALID_ARG;
+  if (nseq < 0) return SPR_ERR_INVALID_ARG;
+  if (p.T > 0 && dpartial == nullptr) return SPR_ERR_INVALID_ARG;
+  if (!aligned16_or_null(dpartial) || !aligned16_or_null(dbias)) return SPR_ERR_ALIGNMENT;
+  if (cu_seqlens != nullptr && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return SPR_ERR_ALIGNMENT;
+  if (p.T > 0) p.dpartial = dpartial;
+  p.dbias = dbias;
+  if (dbias) p.slot_dbias = p.nparts++;
+  p.cu = cu_seqlens;
+  p.nseq = nseq;
+  p.t = t;
+  p.rank = rank;
+  const double pd = static_cast<double>(p_drop);
+  p.drop = p_drop > 0.0f ? 1 : 0;
+  p.scale = static_cast<float>(1.0 / (1.0 - pd));
+  p.thr = static_cast<uint32_t>(std::floor(pd * 4294967296.0));
+  p.key0 = static_cast<uint32_t>(seed);
+  p.key1 = static_cast<uint32_t>(seed >> 32);
   return hip_status(spr::launch_bwd(p, dtype, static_cast<hipStream_t>(stream)));
 }
 

@@ -49,11 +49,13 @@ template <int VPT, bool DRES>
 struct RowBuf {
   u32x4 dy[VPT], z[VPT], dr[DRES ? VPT : 1];
   float mu, rs;
+  uint32_t g_lo, g_hi;   // global token index of the row (dropout backward)
 };
 
-// Stage 1 for block blockIdx.x: dx of its rows, and its [2][h] partial of
-// dgamma/dbeta in the workspace.
-template <class E, int VPT, int RING, bool DRES>
+// Stage 1 for block blockIdx.x: dx of its rows (and, with DROP, dpartial =
+// dx*keep*scale), and its partials of dgamma, dbeta (and dbias) in the
+// workspace: slot j of block b at ws + (b*nparts + j)*h.
+template <class E, int VPT, int RING, bool DRES, bool DROP>
 __device__ __forceinline__ void rows_stage(const BwdParams& p) {
   constexpr int V = E::kVec;
   constexpr int EB = 16 / V;
@@ -72,6 +74,7 @@ __device__ __forceinline__ void rows_stage(const BwdParams& p) {
   int vv[VPT];
   bool valid[VPT];
   float gam[VPT][V], dg[VPT][V], db[VPT][V];
+  float dbs[DROP ? VPT : 1][V];   // dbias running sums
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int v = tid + k * bs;
@@ -80,6 +83,10 @@ __device__ __forceinline__ void rows_stage(const BwdParams& p) {
     unpack(E{}, ld16(static_cast<const char*>(p.gamma) + vv[k] * 16), gam[k]);
 #pragma unroll
     for (int e = 0; e < V; ++e) dg[k][e] = db[k][e] = 0.0f;
+    if constexpr (DROP) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) dbs[k][e] = 0.0f;
+    }
   }
 
   // Rows stream through a ring of RING row buffers: row r + RING is issued
@@ -104,6 +111,12 @@ __device__ __forceinline__ void rows_stage(const BwdParams& p) {
     const int srow = live ? row : r1 - 1;
     b.mu = ln ? p.mean[srow] : 0.0f;
     b.rs = p.rstd[srow];
+    if constexpr (DROP) {
+      // Scalar loads only (ragged offsets): no wait on the ring's vector loads.
+      const uint64_t g = p.drop ? global_token_of(srow, p.T, p.t, p.rank, p.cu, p.nseq) : 0;
+      b.g_lo = static_cast<uint32_t>(g);
+      b.g_hi = static_cast<uint32_t>(g >> 32);
+    }
   };
 
   int parity = 0;
@@ -165,6 +178,23 @@ __device__ __forceinline__ void rows_stage(const BwdParams& p) {
         for (int e = 0; e < V; ++e) dx[e] += f[e];
       }
       st16_dx(static_cast<char*>(p.dx) + off + vv[k] * 16, pack(E{}, dx));
+      if constexpr (DROP) {
+        // Through the dropout: kept channels times the forward's scale, the
+        // forward's own mask (same seed, same global token).
+        float dp[V];
+        if (p.drop) {
+          bool keep[V];
+          dropout_keep<V>(static_cast<uint32_t>(vv[k]), b.g_lo, b.g_hi, p.key0, p.key1, p.thr, keep);
+#pragma unroll
+          for (int e = 0; e < V; ++e) dp[e] = keep[e] ? dx[e] * p.scale : 0.0f;
+        } else {
+#pragma unroll
+          for (int e = 0; e < V; ++e) dp[e] = dx[e];
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) dbs[k][e] += dp[e];
+        st16_dx(static_cast<char*>(p.dpartial) + off + vv[k] * 16, pack(E{}, dp));
+      }
     }
   };
 
@@ -179,24 +209,28 @@ __device__ __forceinline__ void rows_stage(const BwdParams& p) {
     }
   }
 
-  float* wsg = p.ws + static_cast<int64_t>(blockIdx.x) * 2 * h;
-  float* wsb = wsg + h;
+  // Partial slots: dgamma first, then dbeta and dbias where requested.
+  float* ws = p.ws + static_cast<int64_t>(blockIdx.x) * p.nparts * h;
+  auto put = [&](float* dst, const float (&a)[V], int k) {
+#pragma unroll
+    for (int e0 = 0; e0 < V; e0 += 4)
+      st16_ws(dst + vv[k] * V + e0, u32x4{__float_as_uint(a[e0]), __float_as_uint(a[e0 + 1]),
+                                          __float_as_uint(a[e0 + 2]), __float_as_uint(a[e0 + 3])});
+  };
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     if (!valid[k]) continue;
-#pragma unroll
-    for (int e0 = 0; e0 < V; e0 += 4) {
-      st16_ws(wsg + vv[k] * V + e0, u32x4{__float_as_uint(dg[k][e0]), __float_as_uint(dg[k][e0 + 1]),
-                                          __float_as_uint(dg[k][e0 + 2]), __float_as_uint(dg[k][e0 + 3])});
-      st16_ws(wsb + vv[k] * V + e0, u32x4{__float_as_uint(db[k][e0]), __float_as_uint(db[k][e0 + 1]),
-                                          __float_as_uint(db[k][e0 + 2]), __float_as_uint(db[k][e0 + 3])});
+    put(ws, dg[k], k);
+    if (p.slot_dbeta > 0) put(ws + p.slot_dbeta * h, db[k], k);
+    if constexpr (DROP) {
+      if (p.slot_dbias > 0) put(ws + p.slot_dbias * h, dbs[k], k);
     }
   }
 }
 
-template <class E, int VPT, int RING, bool DRES, int MAXBS>
+template <class E, int VPT, int RING, bool DRES, bool DROP, int MAXBS>
 __global__ __launch_bounds__(MAXBS) void sp_region_bwd_rows_kernel(const BwdParams p) {
-  rows_stage<E, VPT, RING, DRES>(p);
+  rows_stage<E, VPT, RING, DRES, DROP>(p);
 }
 
 // Stage 2: the G partials of each column are summed in a fixed tree: 32
@@ -208,13 +242,14 @@ __global__ __launch_bounds__(MAXBS) void sp_region_bwd_rows_kernel(const BwdPara
 constexpr int kGroups = SPR_BWD_GROUPS;
 static_assert(kBwdMaxBlocks % kGroups == 0, "groups must split the partials evenly");
 
-// Column quads [q0, q1) of dgamma/dbeta, cw = blockDim.x / kGroups quads at
-// a time (cw <= CQMAX); thread (group, quad) = (threadIdx.x / cw, threadIdx.x %
-// cw).  Every thread of the block calls this (it has barriers).
-template <int CQMAX>
-__device__ __forceinline__ void reduce_cols(const float* __restrict__ ws, int G, int h, int q0, int q1,
-                                            float* __restrict__ dgamma, float* __restrict__ dbeta) {
-  __shared__ float4 part[2][kGroups][CQMAX];
+// Column quads [q0, q1) of the NP partial slots (block b's slot j at
+// ws + (b*nparts + j)*h) into out[j], cw = blockDim.x / kGroups quads at a
+// time (cw <= CQMAX); thread (group, quad) = (threadIdx.x / cw,
+// threadIdx.x % cw).  Every thread of the block calls this (it has barriers).
+template <int CQMAX, int NP>
+__device__ __forceinline__ void reduce_cols(const float* __restrict__ ws, int G, int h, int nparts, int q0, int q1,
+                                            float* const (&out)[NP]) {
+  __shared__ float4 part[NP][kGroups][CQMAX];
   const int cw = static_cast<int>(blockDim.x) / kGroups;
   const int cq = threadIdx.x % cw;
   const int grp = threadIdx.x / cw;   // < kGroups since blockDim.x = kGroups * cw
@@ -222,38 +257,45 @@ __device__ __forceinline__ void reduce_cols(const float* __restrict__ ws, int G,
   // together, then summed in ascending block order.
   constexpr int kPer = kBwdMaxBlocks / kGroups;
   const int g0 = grp * G / kGroups, g1 = (grp + 1) * G / kGroups;
+  const int64_t bstride = static_cast<int64_t>(nparts) * h;
   for (int qb = q0; qb < q1; qb += cw) {   // block-uniform
     const int c4 = qb + cq;
-    float4 sg = make_float4(0.f, 0.f, 0.f, 0.f), sb = sg;
+    float4 sum[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) sum[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (c4 < q1) {
-      float4 a[kPer], b[kPer];
+      float4 a[NP][kPer];
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         if (g0 + i < g1) {
-          a[i] = reinterpret_cast<const float4*>(ws + static_cast<int64_t>(g0 + i) * 2 * h)[c4];
-          b[i] = reinterpret_cast<const float4*>(ws + static_cast<int64_t>(g0 + i) * 2 * h + h)[c4];
+#pragma unroll
+          for (int j = 0; j < NP; ++j)
+            a[j][i] = reinterpret_cast<const float4*>(ws + (g0 + i) * bstride + static_cast<int64_t>(j) * h)[c4];
         }
       }
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         if (g0 + i < g1) {
-          sg.x += a[i].x; sg.y += a[i].y; sg.z += a[i].z; sg.w += a[i].w;
-          sb.x += b[i].x; sb.y += b[i].y; sb.z += b[i].z; sb.w += b[i].w;
+#pragma unroll
+          for (int j = 0; j < NP; ++j) {
+            sum[j].x += a[j][i].x; sum[j].y += a[j][i].y; sum[j].z += a[j][i].z; sum[j].w += a[j][i].w;
+          }
         }
       }
     }
-    part[0][grp][cq] = sg;
-    part[1][grp][cq] = sb;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) part[j][grp][cq] = sum[j];
     __syncthreads();
     if (grp == 0 && c4 < q1) {
-      float4 tg = part[0][0][cq], tb = part[1][0][cq];
-      for (int i = 1; i < kGroups; ++i) {
-        const float4 a = part[0][i][cq], b = part[1][i][cq];
-        tg.x += a.x; tg.y += a.y; tg.z += a.z; tg.w += a.w;
-        tb.x += b.x; tb.y += b.y; tb.z += b.z; tb.w += b.w;
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        float4 tot = part[j][0][cq];
+        for (int i = 1; i < kGroups; ++i) {
+          const float4 x = part[j][i][cq];
+          tot.x += x.x; tot.y += x.y; tot.z += x.z; tot.w += x.w;
+        }
+        reinterpret_cast<float4*>(out[j])[c4] = tot;
       }
-      reinterpret_cast<float4*>(dgamma)[c4] = tg;
-      if (dbeta) reinterpret_cast<float4*>(dbeta)[c4] = tb;
     }
     __syncthreads();   // part is rewritten by the next chunk
   }
@@ -264,12 +306,20 @@ __device__ __forceinline__ void reduce_cols(const float* __restrict__ ws, int G,
 #endif
 constexpr int kColQuads = SPR_COLS_QPB;
 
+// Outputs of stage 2, slot order (dgamma, then dbeta / dbias where requested).
+struct ColOut {
+  float* p[3];
+};
+
+template <int NP>
 __global__ __launch_bounds__(kColQuads * kGroups) void sp_region_bwd_cols_kernel(const float* __restrict__ ws, int G,
-                                                                                 int h, float* __restrict__ dgamma,
-                                                                                 float* __restrict__ dbeta) {
+                                                                                 int h, int nparts, ColOut o) {
   const int nq = h / 4;
   const int q0 = blockIdx.x * kColQuads;
-  reduce_cols<kColQuads>(ws, G, h, q0, q0 + kColQuads < nq ? q0 + kColQuads : nq, dgamma, dbeta);
+  float* out[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) out[j] = o.p[j];
+  reduce_cols<kColQuads, NP>(ws, G, h, nparts, q0, q0 + kColQuads < nq ? q0 + kColQuads : nq, out);
 }
 
 #ifndef SPR_BWD_MAX_THREADS
@@ -281,32 +331,44 @@ __global__ __launch_bounds__(kColQuads * kGroups) void sp_region_bwd_cols_kernel
 
 // Ring depth per vectors-per-thread, so the packed ring fits the VGPRs the
 // block size leaves (wider rows keep fewer rows in flight).
-template <int VPT, int MAXBS>
+template <int VPT, int MAXBS, bool DROP>
 constexpr int ring_for() {
   return VPT == 1 ? SPR_BWD_RING : (VPT == 2 && MAXBS <= 512 ? SPR_BWD_RING : (VPT == 2 ? 2 : 1));
 }
 
-template <class E, int VPT, bool DRES>
-hipError_t launch_stages(const BwdParams& p, const Shape& sh, hipStream_t stream) {
-  constexpr int MAXBS = SPR_BWD_MAX_THREADS;
-  constexpr int RING = ring_for<VPT, MAXBS>();
-  const dim3 grid(static_cast<unsigned>(p.G)), block(sh.threads);
-  hipLaunchKernelGGL((sp_region_bwd_rows_kernel<E, VPT, RING, DRES, MAXBS>), grid, block, 0, stream, p);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch_cols(const BwdParams& p, hipStream_t stream) {
+  ColOut o{{p.dgamma, nullptr, nullptr}};
+  int np = 1;
+  if (p.slot_dbeta > 0) o.p[np++] = p.dbeta;
+  if (p.slot_dbias > 0) o.p[np++] = p.dbias;
   const int nq = p.h / 4;
-  hipLaunchKernelGGL(sp_region_bwd_cols_kernel, dim3((nq + kColQuads - 1) / kColQuads), dim3(kColQuads * kGroups), 0,
-                     stream, p.ws, p.G, p.h, p.dgamma, p.dbeta);
+  const dim3 grid((nq + kColQuads - 1) / kColQuads), block(kColQuads * kGroups);
+  switch (np) {
+    case 1: hipLaunchKernelGGL(sp_region_bwd_cols_kernel<1>, grid, block, 0, stream, p.ws, p.G, p.h, p.nparts, o); break;
+    case 2: hipLaunchKernelGGL(sp_region_bwd_cols_kernel<2>, grid, block, 0, stream, p.ws, p.G, p.h, p.nparts, o); break;
+    default: hipLaunchKernelGGL(sp_region_bwd_cols_kernel<3>, grid, block, 0, stream, p.ws, p.G, p.h, p.nparts, o); break;
+  }
   return hipGetLastError();
 }
 
-template <class E>
+template <class E, int VPT, bool DRES, bool DROP>
+hipError_t launch_stages(const BwdParams& p, const Shape& sh, hipStream_t stream) {
+  constexpr int MAXBS = SPR_BWD_MAX_THREADS;
+  constexpr int RING = ring_for<VPT, MAXBS, DROP>();
+  const dim3 grid(static_cast<unsigned>(p.G)), block(sh.threads);
+  hipLaunchKernelGGL((sp_region_bwd_rows_kernel<E, VPT, RING, DRES, DROP, MAXBS>), grid, block, 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_cols(p, stream);
+}
+
+template <class E, bool DROP>
 hipError_t launch_rows(const BwdParams& p, const Shape& sh, hipStream_t stream) {
   const bool dres = p.dres != nullptr;
   switch (sh.vpt) {
-    case 1: return dres ? launch_stages<E, 1, true>(p, sh, stream) : launch_stages<E, 1, false>(p, sh, stream);
-    case 2: return dres ? launch_stages<E, 2, true>(p, sh, stream) : launch_stages<E, 2, false>(p, sh, stream);
-    case 4: return dres ? launch_stages<E, 4, true>(p, sh, stream) : launch_stages<E, 4, false>(p, sh, stream);
+    case 1: return dres ? launch_stages<E, 1, true, DROP>(p, sh, stream) : launch_stages<E, 1, false, DROP>(p, sh, stream);
+    case 2: return dres ? launch_stages<E, 2, true, DROP>(p, sh, stream) : launch_stages<E, 2, false, DROP>(p, sh, stream);
+    case 4: return dres ? launch_stages<E, 4, true, DROP>(p, sh, stream) : launch_stages<E, 4, false, DROP>(p, sh, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -328,13 +390,12 @@ Shape bwd_shape(int h, int dtype) {
 hipError_t launch_bwd(const BwdParams& p, int dtype, hipStream_t stream) {
   if (p.G > 0) {
     const Shape sh = bwd_shape(p.h, dtype);
-    return dtype == 1 ? launch_rows<Bf16>(p, sh, stream) : launch_rows<F32>(p, sh, stream);
+    const bool drop = p.dpartial != nullptr;
+    if (dtype == 1) return drop ? launch_rows<Bf16, true>(p, sh, stream) : launch_rows<Bf16, false>(p, sh, stream);
+    return drop ? launch_rows<F32, true>(p, sh, stream) : launch_rows<F32, false>(p, sh, stream);
   }
-  // No rows: dgamma = dbeta = 0 (every group is empty).
-  const int nq = p.h / 4;
-  hipLaunchKernelGGL(sp_region_bwd_cols_kernel, dim3((nq + kColQuads - 1) / kColQuads), dim3(kColQuads * kGroups), 0,
-                     stream, p.ws, p.G, p.h, p.dgamma, p.dbeta);
-  return hipGetLastError();
+  // No rows: every output is 0 (every group of partials is empty).
+  return launch_cols(p, stream);
 }
 
 }  // namespace spr

@@ -38,19 +38,6 @@ namespace {
 #endif
 constexpr int kRowsPerBlockW1 = 4;   // WPR = 1: four independent rows per block
 
-__device__ __forceinline__ uint64_t global_token(const FwdParams& p, int64_t row) {
-  if (p.cu == nullptr) return static_cast<uint64_t>(p.rank) * static_cast<uint64_t>(p.T) + row;
-  // Largest q in [0, nseq) with cu[q] <= row (empty sequences are skipped).
-  int lo = 0, hi = p.nseq;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.cu[mid] <= row) lo = mid; else hi = mid;
-  }
-  const int64_t start = p.cu[lo];
-  const int64_t len = static_cast<int64_t>(p.cu[lo + 1]) - start;
-  return static_cast<uint64_t>(p.t * start + p.rank * len + (row - start));
-}
-
 // Sum over the WPR waves of a row, in wave order (uniform result).
 template <int WPR>
 __device__ __forceinline__ float row_total(float x, float* slot) {
@@ -139,7 +126,7 @@ __global__ __launch_bounds__(WPR == 1 ? 64 * kRowsPerBlockW1 : 64 * WPR, 2) void
     sl.b = ld16(biasp + o);
   };
 
-  const uint64_t g = p.drop ? global_token(p, row) : 0;
+  const uint64_t g = p.drop ? global_token_of(row, p.T, p.t, p.rank, p.cu, p.nseq) : 0;
   const uint32_t g_lo = static_cast<uint32_t>(g), g_hi = static_cast<uint32_t>(g >> 32);
 
   u32x4 zs[ZLDS ? 1 : VPL];   // rounded z, packed (when not in LDS)
@@ -171,17 +158,11 @@ __global__ __launch_bounds__(WPR == 1 ? 64 * kRowsPerBlockW1 : 64 * WPR, 2) void
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[e] = acc[e] + f[e];
     }
-    uint8_t keep[V];
+    bool keep[V];
 #pragma unroll
-    for (int e = 0; e < V; ++e) keep[e] = 1;
+    for (int e = 0; e < V; ++e) keep[e] = true;
     if (p.drop) {
-#pragma unroll
-      for (int b4 = 0; b4 < V / 4; ++b4) {
-        const uint32_t blk = static_cast<uint32_t>(v * (V / 4) + b4);   // channel / 4
-        const Philox4 r = philox4x32_10(blk, g_lo, g_hi, 0u, p.key0, p.key1);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) keep[b4 * 4 + w] = r.w[w] >= p.thr;
-      }
+      dropout_keep<V>(static_cast<uint32_t>(v), g_lo, g_hi, p.key0, p.key1, p.thr, keep);
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[e] = keep[e] ? acc[e] * p.scale : 0.0f;
     }

@@ -99,6 +99,43 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
   return Philox4{{c0, c1, c2, c3}};
 }
 
+// Keep decisions of the V channels of 16-byte vector v of the row with global
+// token index g: channel j is kept iff word (j mod 4) of Philox-4x32-10 with
+// counter (j div 4, lo32 g, hi32 g, 0) and key (k0, k1) is >= thr.
+template <int V>
+__device__ __forceinline__ void dropout_keep(uint32_t v, uint32_t g_lo, uint32_t g_hi, uint32_t k0, uint32_t k1,
+                                             uint32_t thr, bool* keep) {
+#pragma unroll
+  for (int b4 = 0; b4 < V / 4; ++b4) {
+    const Philox4 r = philox4x32_10(v * (V / 4) + b4, g_lo, g_hi, 0u, k0, k1);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) keep[b4 * 4 + w] = r.w[w] >= thr;
+  }
+}
+
+// Global token index of local row `row` (its row in the unsharded [s*b][h]
+// view): rank*T + row for a uniform shard; for a packed ragged batch with
+// local offsets cu[0..nseq], row i of sequence q is token
+// t*cu[q] + rank*(cu[q+1]-cu[q]) + (i-cu[q]).  The offsets are read through
+// the constant address space, so the lookups are scalar loads: they are
+// counted apart from the vector-memory stream and never make a wait on them
+// drain the prefetched rows.
+__device__ __forceinline__ uint64_t global_token_of(int64_t row, int64_t T, int t, int rank, const int32_t* cu,
+                                                    int nseq) {
+  if (cu == nullptr) return static_cast<uint64_t>(rank) * static_cast<uint64_t>(T) + row;
+  typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+  const const_i32p c = (const_i32p)(cu);   // address-space cast (generic -> constant)
+  // Largest q in [0, nseq) with cu[q] <= row (empty sequences are skipped).
+  int lo = 0, hi = nseq;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (c[mid] <= row) lo = mid; else hi = mid;
+  }
+  const int64_t start = c[lo];
+  const int64_t len = static_cast<int64_t>(c[lo + 1]) - start;
+  return static_cast<uint64_t>(t * start + rank * len + (row - start));
+}
+
 // ---------------------------------------------------------------------------
 // Reductions.  Wave sums use DPP row steps plus readlane (below), and the
 // cross-wave stage sums the per-wave totals in wave order, so a block's

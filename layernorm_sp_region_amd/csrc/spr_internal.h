@@ -41,13 +41,30 @@ struct BwdParams {
   const void* gamma;
   const void* dres;       // [T][h] or null
   void* dx;
-  float* ws;              // [G][2][h]
+  float* ws;              // [G][nparts][h]
   float* dgamma;
   float* dbeta;           // null allowed
   int64_t T;
   int32_t h;
   int32_t norm;
   int32_t G;
+  // Partial slots per block: dgamma in slot 0, dbeta / dbias in slot_dbeta /
+  // slot_dbias (0: not computed).
+  int32_t nparts;
+  int32_t slot_dbeta;
+  int32_t slot_dbias;
+  // Dropout backward (dpartial != null): dpartial = dx * keep * scale and the
+  // dbias partials, with the forward's mask parameters.
+  void* dpartial;         // [T][h] or null
+  float* dbias;           // [h] or null
+  const int32_t* cu;      // [nseq+1] local offsets or null (uniform shard)
+  int32_t nseq;
+  int32_t t;
+  int32_t rank;
+  int32_t drop;           // p > 0
+  uint32_t thr;
+  float scale;
+  uint32_t key0, key1;
 };
 
 // Number of row blocks of the backward's first stage (and of workspace

@@ -163,6 +163,49 @@ def test_bwd_rejects(lib, over, status):
     assert call_bwd(lib, bwd_args(**over)) == status
 
 
+def bwd_dropout_args(**over):
+    a = dict(bwd_args(ws_bytes=64 * 3 * 512 * 4), p=0.1, rank=1, seed=7, cu=None, nseq=0, dpartial=P, dbias=P)
+    a.update(over)
+    return a
+
+
+def call_bwd_dropout(lib, a):
+    return lib.sp_region_bwd_dropout(a["b"], a["s"], a["h"], a["t"], a["gamma"], a["norm"], a["dtype"], a["dy"],
+                                     a["z"], a["mean"], a["rstd"], a["dres"], a["p"], a["rank"], a["seed"], a["cu"],
+                                     a["nseq"], a["dx"], a["dpartial"], a["dgamma"], a["dbeta"], a["dbias"], a["ws"],
+                                     a["ws_bytes"], a["stream"])
+
+
+BWD_DROPOUT_CASES = BWD_CASES[2:] + [
+    (dict(ws_bytes=64 * 3 * 512 * 4 - 1), INVALID),          # three partial slots per block
+    (dict(ws_bytes=64 * 2 * 512 * 4), INVALID),
+    (dict(ws=None), INVALID),
+    (dict(dpartial=None), INVALID),
+    (dict(p=1.0), INVALID), (dict(p=-0.1), INVALID), (dict(p=float("nan")), INVALID),
+    (dict(rank=4), INVALID), (dict(rank=-1), INVALID),
+    (dict(cu=P, nseq=0), INVALID), (dict(cu=P, nseq=2, b=2), INVALID), (dict(nseq=-1), INVALID),
+    (dict(cu=P + 2, nseq=1), ALIGN), (dict(dpartial=P + 4), ALIGN), (dict(dbias=P + 8), ALIGN),
+]
+
+
+@pytest.mark.parametrize("over,status", BWD_DROPOUT_CASES, ids=[str(c[0]) for c in BWD_DROPOUT_CASES])
+def test_bwd_dropout_rejects(lib, over, status):
+    assert call_bwd_dropout(lib, bwd_dropout_args(**over)) == status
+
+
+def test_bwd_dropout_workspace_bytes(lib):
+    ws3, ws2 = lib.sp_region_bwd_dropout_workspace_bytes, lib.sp_region_bwd_workspace_bytes
+    assert ws3(0, 64) == 0 and ws3(5, 0) == 0
+    for T, h in [(64, 512), (2048, 8192), (100000, 5120), (1, 8)]:
+        assert ws3(T, h) * 2 == ws2(T, h) * 3
+
+
+def test_bwd_dropout_empty_shard_needs_no_outputs(lib):
+    # T = 0: nothing to launch beyond the zero-filled parameter gradients, which
+    # need a device; without one only the argument checks can be exercised.
+    assert call_bwd_dropout(lib, bwd_dropout_args(s=0, dpartial=None, ws=None, ws_bytes=0, p=2.0)) == INVALID
+
+
 def test_copy_rejects(lib):
     assert lib.sp_region_hbm_copy(P, P, 15, None) == INVALID
     assert lib.sp_region_hbm_copy(None, P, 16, None) == INVALID

@@ -1,0 +1,118 @@
+"""GPU parity of the backward through the dropout and the slab sum
+(sp_region_bwd_dropout) against the oracle's dropout_backward on the same
+seeded inputs.
+
+Bars: dpartial as dx (bf16: half an ulp of the float64 value plus a float32
+slack of 4e-5*(1+|ref|), and 2e-2 absolute below 8; float32: 1e-4 relative),
+exactly 0 wherever the forward dropped; dbias_j within 1e-4 * sum_i
+|dpartial_ij|.  dx, dgamma and dbeta must equal sp_region_bwd's bit for bit.
+"""
+import numpy as np
+import pytest
+
+import layernorm_sp_region_amd as spr
+import oracle.region as ref
+import workloads as W
+from test_gpu_parity import assert_out_close, inputs_for, log, to_np_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_both(inp, w, rank, device, dres=None, recommended_stride=True):
+    import torch
+    t = lambda a: W.as_torch(a, device)
+    P = t(inp["partials"])
+    if recommended_stride:
+        Pp = spr.empty_partials(P.shape[0], P.shape[1], P.shape[2], P.dtype, device)
+        Pp.copy_(P)
+        P = Pp
+    cu = inp["cu_seqlens"]
+    fo = spr.fwd(P, t(inp["gamma"]), t(inp["beta"]), bias=t(inp["bias"]), residual=t(inp["residual"]),
+                 b=inp["b"], s=inp["s"], t=w.t, rank=rank, eps=w.eps, p_drop=w.p_drop, seed=inp["seed"],
+                 norm=w.norm, cu_seqlens=cu)
+    dy, gamma, dr = t(inp["dy"]), t(inp["gamma"]), t(dres)
+    one = spr.bwd(dy, fo.z, fo.mean, fo.rstd, gamma, b=inp["b"], s=inp["s"], t=w.t, norm=w.norm, dres_in=dr)
+    two = spr.bwd_dropout(dy, fo.z, fo.mean, fo.rstd, gamma, b=inp["b"], s=inp["s"], t=w.t, rank=rank,
+                          p_drop=w.p_drop, seed=inp["seed"], norm=w.norm, cu_seqlens=cu, dres_in=dr)
+    torch.cuda.synchronize()
+    bits = lambda x: None if x is None else x.view(torch.int32 if x.dtype == torch.float32 else torch.int16).cpu()
+    for name in ("dx", "dgamma", "dbeta"):
+        a, b = getattr(one, name), getattr(two, name)
+        assert (a is None) == (b is None), name
+        if a is not None:
+            assert torch.equal(bits(a), bits(b)), f"{name} differs from sp_region_bwd"
+    return fo, two
+
+
+def check(w, inp, rank, two, dres=None):
+    o = ref.region_forward(inp["partials"], t=w.t, rank=rank, dtype=w.dtype, norm=w.norm, eps=w.eps,
+                           p_drop=w.p_drop, seed=inp["seed"], gamma=inp["gamma"], beta=inp["beta"],
+                           bias=inp["bias"], residual=inp["residual"], cu_seqlens=inp["cu_seqlens"])
+    ob = ref.region_backward(inp["dy"], o["z"], inp["gamma"], dtype=w.dtype, norm=w.norm, eps=w.eps, dres_in=dres)
+    od = ref.dropout_backward(ob["dx"], t=w.t, rank=rank, p_drop=w.p_drop, seed=inp["seed"],
+                              cu_seqlens=inp["cu_seqlens"])
+    got = to_np_f64(two.dpartial)
+    assert np.all(got[~od["keep"]] == 0.0), "dpartial nonzero where the forward dropped"
+    assert_out_close(got, od["dpartial"], w.dtype, "dpartial", 4e-5)
+    assert_out_close(to_np_f64(two.dx), ob["dx"], w.dtype, "dx", 3e-5)
+    err = np.abs(to_np_f64(two.dbias) - od["dbias"])
+    assert np.all(err <= 1e-4 * od["C"]), f"dbias: worst err/C {np.max(err / np.maximum(od['C'], 1e-300)):.2e}"
+    log(f"  dropout backward ok: dbias err/C max {np.max(err / np.maximum(od['C'], 1e-300)):.2e}, "
+        f"dropped {(~od['keep']).mean():.4f}")
+
+
+@pytest.mark.parametrize("name,rank", [("tiny", 3), ("page_demo", 7), ("shard70b", 0), ("ragged13b", 5)])
+def test_workload_dropout_backward(cuda_device, name, rank):
+    w = W.BY_NAME[name]
+    log(f"[dropout-bwd] {name} rank={rank}")
+    inp = inputs_for(w)
+    _, two = run_both(inp, w, rank, cuda_device)
+    check(w, inp, rank, two)
+
+
+EDGE = [
+    # ragged shard with dropout on: the token index comes from cu_seqlens (scalar loads)
+    (W.custom("ragged_drop", h=1024, t=4, lengths=(40, 0, 96, 8, 200), norm="layernorm", p_drop=0.3), 2, True),
+    # odd t, 65 vectors per row (a partial wave), b = 2, extra gradient on z
+    (W.custom("odd_t3_h520", h=520, t=3, s=3 * 37, b=2, p_drop=0.25), 1, True),
+    # largest bf16 h: 4 vectors per thread (the register-heavy variant)
+    (W.custom("hmax_bf16_t5", h=16384, t=5, s=5 * 16, p_drop=0.1), 4, True),
+    # float32 RMSNorm, p = 0.5, no extra gradient
+    (W.custom("f32_rms_p05", h=768, t=2, s=2 * 50, dtype="f32", norm="rmsnorm", p_drop=0.5), 1, False),
+]
+
+
+@pytest.mark.parametrize("w,rank,with_dres", EDGE, ids=[e[0].name for e in EDGE])
+def test_edge_dropout_backward(cuda_device, w, rank, with_dres):
+    log(f"[dropout-bwd-edge] {w.name} rank={rank} dres={with_dres}")
+    inp = W.make_inputs(w)
+    dres = None
+    if with_dres:
+        # a [T][h] gradient in the storage dtype (T rows of a uniform shard of the same width)
+        dres = W.make_inputs(W.custom(w.name + "_g", h=w.h, t=w.t, s=w.t * inp["T"], dtype=w.dtype, seed=97))["dy"]
+        assert dres.shape == (inp["T"], w.h)
+    _, two = run_both(inp, w, rank, cuda_device, dres=dres)
+    check(w, inp, rank, two, dres=dres)
+
+
+def test_no_dropout_gives_dx(cuda_device):
+    """p = 0: dpartial is dx's own bits (no mask, no scale)."""
+    import torch
+    w = W.BY_NAME["ragged13b"]
+    inp = inputs_for(w)
+    _, two = run_both(inp, w, 0, cuda_device, recommended_stride=False)
+    assert w.p_drop == 0.0
+    assert torch.equal(two.dx.view(torch.int16), two.dpartial.view(torch.int16))
+
+
+def test_empty_shard_dropout_backward(cuda_device):
+    import torch
+    w = W.custom("empty", h=64, t=4, s=0)
+    inp = W.make_inputs(w)
+    t = lambda a: W.as_torch(a, cuda_device)
+    z = torch.empty((0, 64), dtype=torch.bfloat16, device=cuda_device)
+    st = torch.empty(0, device=cuda_device)
+    out = spr.bwd_dropout(z, z, st, st, t(inp["gamma"]), b=1, s=0, t=4, rank=1, p_drop=0.2, seed=3)
+    torch.cuda.synchronize()
+    for g in (out.dgamma, out.dbeta, out.dbias):
+        assert torch.all(g == 0)
