@@ -325,11 +325,17 @@ def traffic_summary(fetch_dir, write_dir, copy_bytes=1 << 30):
     lines = [f"# FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f} "
              f"(1 GiB calibration copy: counter KiB vs true KiB)"]
     fwd = None
-    for key in ("sp_region_fwd_kernel", "sp_region_bwd_rows_kernel", "sp_region_bwd_cols_kernel"):
-        fb = pick(fe, key) * f_scale * 1024
-        wb = pick(wr, key) * w_scale * 1024
-        lines.append(f"{key}: fetch_bytes={fb:.0f} write_bytes={wb:.0f} total_bytes={fb + wb:.0f}")
-        if key == "sp_region_fwd_kernel":
+    # One line per kernel instantiation (the rows kernel with and without the
+    # dropout backward are different kernels), in the order of the path.
+    order = ("sp_region_fwd_kernel", "sp_region_bwd_rows_kernel", "sp_region_bwd_cols_kernel")
+    names = sorted((k for k in fe if any(o in k for o in order) and k in wr),
+                   key=lambda k: (next(i for i, o in enumerate(order) if o in k), k))
+    for key in names:
+        fb = fe[key] * f_scale * 1024
+        wb = wr[key] * w_scale * 1024
+        short = key.replace("spr::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        lines.append(f"{short}: fetch_bytes={fb:.0f} write_bytes={wb:.0f} total_bytes={fb + wb:.0f}")
+        if "sp_region_fwd_kernel" in key and fwd is None:
             fwd = fb + wb
     lines.append(f"kernel_source_sha256={kernel_source_hash()}")
     lines.append(f"hbm_bytes_per_launch={fwd:.0f}")

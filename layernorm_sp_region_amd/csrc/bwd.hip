@@ -263,23 +263,28 @@ __device__ __forceinline__ void reduce_cols(const float* __restrict__ ws, int G,
     float4 sum[NP];
 #pragma unroll
     for (int j = 0; j < NP; ++j) sum[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c4 < q1) {
+    if (G > 0) {   // block-uniform; G == 0: no partials exist (the sums stay 0)
+      // Every load is unconditional, from a clamped in-bounds address (a
+      // load under a branch would make the waitcnt pass serialise them);
+      // the bounds are applied by the selects below.
+      const int cc = c4 < q1 ? c4 : q1 - 1;
       float4 a[NP][kPer];
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        if (g0 + i < g1) {
+        const int gi = g0 + i < G ? g0 + i : G - 1;
 #pragma unroll
-          for (int j = 0; j < NP; ++j)
-            a[j][i] = reinterpret_cast<const float4*>(ws + (g0 + i) * bstride + static_cast<int64_t>(j) * h)[c4];
-        }
+        for (int j = 0; j < NP; ++j)
+          a[j][i] = reinterpret_cast<const float4*>(ws + gi * bstride + static_cast<int64_t>(j) * h)[cc];
       }
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        if (g0 + i < g1) {
+        const bool in = g0 + i < g1;
 #pragma unroll
-          for (int j = 0; j < NP; ++j) {
-            sum[j].x += a[j][i].x; sum[j].y += a[j][i].y; sum[j].z += a[j][i].z; sum[j].w += a[j][i].w;
-          }
+        for (int j = 0; j < NP; ++j) {
+          sum[j].x = in ? sum[j].x + a[j][i].x : sum[j].x;
+          sum[j].y = in ? sum[j].y + a[j][i].y : sum[j].y;
+          sum[j].z = in ? sum[j].z + a[j][i].z : sum[j].z;
+          sum[j].w = in ? sum[j].w + a[j][i].w : sum[j].w;
         }
       }
     }
