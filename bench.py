@@ -91,6 +91,42 @@ def read_traffic():
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle, as it is, on a bounded sample of the workload.
 # ---------------------------------------------------------------------------
+def plan_timing(W, n=1024, t=8, reps=200):
+    """Host-side batch planning (library, then the oracle beside it) on a
+    seeded batch of n sequences with the ragged workload's length mix
+    (lognormal, mean 4096, CV 0.18): buckets at CV 0.15, the SP gate of each
+    bucket and its padded shard layout."""
+    import numpy as np
+    import layernorm_sp_region_amd as spr
+    import oracle.batching as OB
+    w = W.BY_NAME["ragged13b"]
+    rng = np.random.default_rng(w.input_seed + 7)
+    lens = [int(v) for v in np.maximum(1, np.rint(4096 * rng.lognormal(-0.016, 0.1786, n)))]
+
+    def run(bucket, gate, layout):
+        order, starts = bucket(lens)
+        nsp = 0
+        for a, b in zip(starts, starts[1:]):
+            bk = [lens[i] for i in order[a:b]]
+            if gate(bk, 0.0):
+                layout(bk, t)
+                nsp += 1
+        return len(starts) - 1, nsp
+
+    nb, nsp = run(spr.bucket_by_tokens, spr.sp_gate, spr.shard_layout)
+    assert (nb, nsp) == run(OB.bucket_by_tokens, OB.sp_gate, OB.shard_layout)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run(spr.bucket_by_tokens, spr.sp_gate, spr.shard_layout)
+    lib_us = (time.perf_counter() - t0) / reps * 1e6
+    t0 = time.perf_counter()
+    for _ in range(max(1, reps // 20)):
+        run(OB.bucket_by_tokens, OB.sp_gate, OB.shard_layout)
+    oracle_us = (time.perf_counter() - t0) / max(1, reps // 20) * 1e6
+    return {"sequences": n, "t": t, "buckets": nb, "sp_buckets": nsp, "us_per_batch": lib_us,
+            "oracle_us_per_batch": oracle_us}
+
+
 def cpu_baseline(w, inp, budget_s=12.0, chunk=64):
     import numpy as np
     import oracle.region as ref
@@ -238,6 +274,7 @@ def run(args):
            f"({elapsed_ev / args.steps * 1e6:.1f} with events); fwd {achieved:.0f} GB/s, "
            f"fwd+bwd {(fb + bb) / ((fwd_ms.mean() + bwd_ms.mean()) * 1e-3) / 1e9:.0f} GB/s")
 
+    plan = plan_timing(W)
     traffic = read_traffic()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp)
     kernel_us = (fwd_ms.mean() + bwd_ms.mean()) * 1e3
@@ -269,6 +306,7 @@ def run(args):
         "roofline": {"kernel": "sp_region_fwd_kernel", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "cpu_baseline": cpu,
+        "host_planning": plan,
     }
     print(json.dumps(rec), flush=True)
 

@@ -217,6 +217,63 @@ int sp_region_bwd_dropout(int64_t b, int64_t s, int64_t h, int32_t t,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* ------------------------------------------------------------------------
+ * Host-side batch planning (no device work; pointers are HOST pointers).
+ *
+ * coreui.cn, "Why Sequence Parallel saves memory but makes throughput
+ * jitter: from reduce-scatter to the LayerNorm boundary", section "stabilise
+ * the shapes first, then define the LayerNorm shard contract": the step
+ * function buckets the batch by length with a length coefficient of
+ * variation (CV) of at most 0.15 and runs a bucket with tensor parallelism
+ * alone when its CV exceeds 0.18 or the reduce-scatter wait share exceeds
+ * 0.22.  CV = population standard deviation / mean of the sequence lengths
+ * (0 for an empty or all-zero set).  CV thresholds are integers in basis
+ * points (1500 = 0.15), and "CV <= c" is decided exactly in integer
+ * arithmetic:  1e8 * (n*sum(x^2) - sum(x)^2) <= c_bp^2 * sum(x)^2.
+ * Limits: n <= 2^20 sequences, 0 <= length <= 2^24, 0 <= c_bp <= 100000.
+ * Arguments outside them, or NULL outputs, return SPR_ERR_INVALID_ARG and
+ * write nothing.
+ * ------------------------------------------------------------------------ */
+#define SPR_MAX_CV_BP 1500          /* bucket_by_tokens(max_cv = 0.15) */
+#define SPR_GATE_CV_BP 1800         /* TP alone above a bucket length CV of 0.18 */
+#define SPR_GATE_RS_WAIT 0.22       /* ... or above a reduce-scatter wait share of 0.22 */
+
+/* *within = 1 iff CV(lengths[0..n)) <= cv_bp / 10^4. */
+int sp_region_cv_within(const int32_t* lengths, int32_t n, int32_t cv_bp, int32_t* within);
+
+/*
+ * Length buckets: the batch sorted by (length, index) and cut greedily, the
+ * next sequence joining the current bucket while the bucket's CV stays
+ * <= max_cv_bp and, if max_tokens > 0, its token total stays <= max_tokens;
+ * the first sequence of a bucket always joins it.
+ *   order         out [n]: sequence indices, bucket by bucket.
+ *   bucket_start  out [n+1]: bucket k is order[bucket_start[k] ..
+ *                 bucket_start[k+1]); entries 0..*n_buckets are written.
+ *   n_buckets     out.
+ */
+int sp_region_bucket_by_tokens(const int32_t* lengths, int32_t n, int32_t max_cv_bp, int64_t max_tokens,
+                               int32_t* order, int32_t* bucket_start, int32_t* n_buckets);
+
+/*
+ * SP gate of one bucket: *use_sp = 1 iff CV(lengths) <= max_cv_bp / 10^4 and
+ * rs_wait_share <= max_rs_wait_share (SPR_GATE_CV_BP and SPR_GATE_RS_WAIT are
+ * the page's values); 0 means run the bucket with tensor parallelism alone.
+ * NaN shares are invalid.
+ */
+int sp_region_sp_gate(const int32_t* lengths, int32_t n, double rs_wait_share, int32_t max_cv_bp,
+                      double max_rs_wait_share, int32_t* use_sp);
+
+/*
+ * Packed shard layout of a bucket for TP degree t (1..SPR_MAX_T_SLABS): each
+ * sequence is padded up to a multiple of t (padded[q]); rank r holds the
+ * r-th of the t equal slices of every sequence, so every rank has the same
+ * T = sum(padded)/t local rows, and cu_local [n+1] are the local row offsets
+ * that sp_region_fwd / sp_region_bwd_dropout take as cu_seqlens (with b = 1,
+ * s = sum(padded)).  T beyond INT32_MAX returns SPR_ERR_UNSUPPORTED.
+ */
+int sp_region_shard_layout(const int32_t* lengths, int32_t n, int32_t t, int32_t* padded, int32_t* cu_local,
+                           int64_t* n_local_tokens);
+
 /*
  * Calibration kernel: copies nbytes (a multiple of 16) from src to dst with
  * 16-byte loads and stores, for measuring the achievable HBM copy rate and for

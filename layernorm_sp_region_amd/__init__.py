@@ -45,6 +45,10 @@ SIGNATURES = {
                                              _F32, _I32, _U64, _VP, _I32,
                                              _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "sp_region_hbm_copy": (ctypes.c_int, [_VP, _VP, _SZ, _VP]),
+    "sp_region_cv_within": (ctypes.c_int, [_VP, _I32, _I32, _VP]),
+    "sp_region_bucket_by_tokens": (ctypes.c_int, [_VP, _I32, _I32, _I64, _VP, _VP, _VP]),
+    "sp_region_sp_gate": (ctypes.c_int, [_VP, _I32, ctypes.c_double, _I32, ctypes.c_double, _VP]),
+    "sp_region_shard_layout": (ctypes.c_int, [_VP, _I32, _I32, _VP, _VP, _VP]),
 }
 
 _lib = None
@@ -334,3 +338,66 @@ def hbm_copy(src, dst) -> None:
         raise ValueError("src and dst sizes differ")
     stream = torch.cuda.current_stream(src.device).cuda_stream
     _check("sp_region_hbm_copy", lib.sp_region_hbm_copy(src.data_ptr(), dst.data_ptr(), n, stream))
+
+
+# ---------------------------------------------------------------------------
+# Host-side batch planning (argument marshalling only; the library decides).
+# ---------------------------------------------------------------------------
+MAX_CV_BP = 1500
+GATE_CV_BP = 1800
+GATE_RS_WAIT = 0.22
+
+
+def _lengths_array(lengths):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(lengths, dtype=np.int64))
+    if a.ndim != 1:
+        raise ValueError("lengths must be one-dimensional")
+    if a.size and (a.min() < 0 or a.max() > 2 ** 31 - 1):
+        raise ValueError("lengths out of range")
+    return np.ascontiguousarray(a.astype(np.int32))
+
+
+def cv_within(lengths, cv_bp: int) -> bool:
+    import numpy as np
+    a = _lengths_array(lengths)
+    out = np.zeros(1, dtype=np.int32)
+    _check("sp_region_cv_within", load_library().sp_region_cv_within(a.ctypes.data, a.size, cv_bp, out.ctypes.data))
+    return bool(out[0])
+
+
+def bucket_by_tokens(lengths, max_cv_bp: int = MAX_CV_BP, max_tokens: int = 0):
+    """(order, starts): bucket k is order[starts[k]:starts[k+1]]."""
+    import numpy as np
+    a = _lengths_array(lengths)
+    order = np.zeros(max(a.size, 1), dtype=np.int32)
+    starts = np.zeros(a.size + 1, dtype=np.int32)
+    nb = np.zeros(1, dtype=np.int32)
+    st = load_library().sp_region_bucket_by_tokens(a.ctypes.data, a.size, max_cv_bp, max_tokens, order.ctypes.data,
+                                                   starts.ctypes.data, nb.ctypes.data)
+    _check("sp_region_bucket_by_tokens", st)
+    return order[:a.size].tolist(), starts[:nb[0] + 1].tolist()
+
+
+def sp_gate(lengths, rs_wait_share: float, max_cv_bp: int = GATE_CV_BP,
+            max_rs_wait_share: float = GATE_RS_WAIT) -> bool:
+    import numpy as np
+    a = _lengths_array(lengths)
+    out = np.zeros(1, dtype=np.int32)
+    st = load_library().sp_region_sp_gate(a.ctypes.data, a.size, float(rs_wait_share), max_cv_bp,
+                                          float(max_rs_wait_share), out.ctypes.data)
+    _check("sp_region_sp_gate", st)
+    return bool(out[0])
+
+
+def shard_layout(lengths, t: int):
+    """(padded lengths, local cu_seqlens, local token count T)."""
+    import numpy as np
+    a = _lengths_array(lengths)
+    padded = np.zeros(max(a.size, 1), dtype=np.int32)
+    cu = np.zeros(a.size + 1, dtype=np.int32)
+    T = np.zeros(1, dtype=np.int64)
+    st = load_library().sp_region_shard_layout(a.ctypes.data, a.size, t, padded.ctypes.data, cu.ctypes.data,
+                                               T.ctypes.data)
+    _check("sp_region_shard_layout", st)
+    return padded[:a.size].tolist(), cu.tolist(), int(T[0])

@@ -116,3 +116,32 @@ def test_empty_shard_dropout_backward(cuda_device):
     torch.cuda.synchronize()
     for g in (out.dgamma, out.dbeta, out.dbias):
         assert torch.all(g == 0)
+
+
+def test_planned_buckets_end_to_end(cuda_device):
+    """Host planning feeds the region: a mixed batch is bucketed at CV 0.15,
+    each bucket that passes the gate is laid out for t = 4 (padded lengths,
+    local cu_seqlens from the library), and the forward plus the dropout
+    backward run on that layout match the oracle."""
+    import torch
+    from test_gpu_parity import compare, run_gpu
+    lens = [37, 4096, 45, 3900, 41, 4200, 39, 4001, 0]
+    order, starts = spr.bucket_by_tokens(lens)
+    assert not spr.sp_gate(lens, 0.0) and len(starts) >= 3
+    ran = 0
+    for a, b in zip(starts, starts[1:]):
+        bucket = [lens[i] for i in order[a:b]]
+        if not spr.sp_gate(bucket, 0.05) or sum(bucket) == 0:
+            continue
+        padded, cu, T = spr.shard_layout(bucket, 4)
+        w = W.custom(f"bucket{a}", h=512, t=4, lengths=tuple(padded), p_drop=0.2)
+        inp = W.make_inputs(w)
+        assert inp["T"] == T and [int(c) for c in inp["cu_seqlens"]] == cu
+        log(f"[planned] bucket {bucket} -> T={T}")
+        gpu = run_gpu(inp, w, 3, cuda_device)
+        compare(w, inp, gpu, 3)
+        _, two = run_both(inp, w, 3, cuda_device)
+        check(w, inp, 3, two)
+        torch.cuda.synchronize()
+        ran += 1
+    assert ran >= 2
