@@ -137,9 +137,12 @@ int sp_region_fwd(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p
 
 /*
  * Bytes of device workspace sp_region_bwd needs for n_local_tokens = T rows of
- * h channels: a float32 [G][2][h] array of per-block dgamma/dbeta partial sums,
- * G a fixed function of (T, h).  A pure function (no device query).  Returns 0
- * for T <= 0 or h <= 0.
+ * h channels: float32 dgamma/dbeta partial sums of G = min(T, 256) row blocks,
+ * two slots of h per block.  Slots and blocks sit at strides 1 KiB past a
+ * multiple of 2 KiB (slot: round_up(h, 512) + 256 floats; block:
+ * round_up(2*slot, 512) + 256 floats), so the blocks' simultaneous partial
+ * writes spread over the HBM channels.  A pure function (no device query).
+ * Returns 0 for T <= 0 or h <= 0.
  */
 size_t sp_region_bwd_workspace_bytes(int64_t n_local_tokens, int64_t h);
 
@@ -176,8 +179,9 @@ int sp_region_bwd(int64_t b, int64_t s, int64_t h, int32_t t,
 
 /*
  * Bytes of device workspace sp_region_bwd_dropout needs for T rows of h
- * channels: float32 [G][3][h] (dgamma, dbeta and dbias partials), G as for
- * sp_region_bwd_workspace_bytes.  A pure function; 0 for T <= 0 or h <= 0.
+ * channels: as sp_region_bwd_workspace_bytes with three slots per block
+ * (dgamma, dbeta and dbias partials; block stride round_up(3*slot, 512) + 256
+ * floats).  A pure function; 0 for T <= 0 or h <= 0.
  */
 size_t sp_region_bwd_dropout_workspace_bytes(int64_t n_local_tokens, int64_t h);
 

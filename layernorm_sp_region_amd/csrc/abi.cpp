@@ -126,12 +126,14 @@ int64_t sp_region_partials_stride(int64_t n_local_tokens, int64_t h, int32_t dty
 
 size_t sp_region_bwd_workspace_bytes(int64_t n_local_tokens, int64_t h) {
   if (n_local_tokens <= 0 || h <= 0) return 0;
-  return static_cast<size_t>(spr::bwd_blocks(n_local_tokens, h)) * 2u * static_cast<size_t>(h) * sizeof(float);
+  return static_cast<size_t>(spr::bwd_blocks(n_local_tokens, h)) * static_cast<size_t>(spr::ws_block_stride(h, 2)) *
+         sizeof(float);
 }
 
 size_t sp_region_bwd_dropout_workspace_bytes(int64_t n_local_tokens, int64_t h) {
   if (n_local_tokens <= 0 || h <= 0) return 0;
-  return static_cast<size_t>(spr::bwd_blocks(n_local_tokens, h)) * 3u * static_cast<size_t>(h) * sizeof(float);
+  return static_cast<size_t>(spr::bwd_blocks(n_local_tokens, h)) * static_cast<size_t>(spr::ws_block_stride(h, 3)) *
+         sizeof(float);
 }
 
 }  // extern "C"

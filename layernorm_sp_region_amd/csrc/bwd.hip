@@ -54,7 +54,7 @@ struct RowBuf {
 
 // Stage 1 for block blockIdx.x: dx of its rows (and, with DROP, dpartial =
 // dx*keep*scale), and its partials of dgamma, dbeta (and dbias) in the
-// workspace: slot j of block b at ws + (b*nparts + j)*h.
+// workspace: slot j of block b at ws + b*ws_bstride + j*ws_sstride.
 template <class E, int VPT, int RING, bool DRES, bool DROP>
 __device__ __forceinline__ void rows_stage(const BwdParams& p) {
   constexpr int V = E::kVec;
@@ -210,7 +210,7 @@ __device__ __forceinline__ void rows_stage(const BwdParams& p) {
   }
 
   // Partial slots: dgamma first, then dbeta and dbias where requested.
-  float* ws = p.ws + static_cast<int64_t>(blockIdx.x) * p.nparts * h;
+  float* ws = p.ws + static_cast<int64_t>(blockIdx.x) * p.ws_bstride;
   auto put = [&](float* dst, const float (&a)[V], int k) {
 #pragma unroll
     for (int e0 = 0; e0 < V; e0 += 4)
@@ -221,9 +221,9 @@ __device__ __forceinline__ void rows_stage(const BwdParams& p) {
   for (int k = 0; k < VPT; ++k) {
     if (!valid[k]) continue;
     put(ws, dg[k], k);
-    if (p.slot_dbeta > 0) put(ws + p.slot_dbeta * h, db[k], k);
+    if (p.slot_dbeta > 0) put(ws + p.slot_dbeta * p.ws_sstride, db[k], k);
     if constexpr (DROP) {
-      if (p.slot_dbias > 0) put(ws + p.slot_dbias * h, dbs[k], k);
+      if (p.slot_dbias > 0) put(ws + p.slot_dbias * p.ws_sstride, dbs[k], k);
     }
   }
 }
@@ -243,11 +243,12 @@ constexpr int kGroups = SPR_BWD_GROUPS;
 static_assert(kBwdMaxBlocks % kGroups == 0, "groups must split the partials evenly");
 
 // Column quads [q0, q1) of the NP partial slots (block b's slot j at
-// ws + (b*nparts + j)*h) into out[j], cw = blockDim.x / kGroups quads at a
+// ws + b*bstride + j*sstride) into out[j], cw = blockDim.x / kGroups quads at a
 // time (cw <= CQMAX); thread (group, quad) = (threadIdx.x / cw,
 // threadIdx.x % cw).  Every thread of the block calls this (it has barriers).
 template <int CQMAX, int NP>
-__device__ __forceinline__ void reduce_cols(const float* __restrict__ ws, int G, int h, int nparts, int q0, int q1,
+__device__ __forceinline__ void reduce_cols(const float* __restrict__ ws, int G, int64_t bstride, int64_t sstride,
+                                            int q0, int q1,
                                             float* const (&out)[NP]) {
   __shared__ float4 part[NP][kGroups][CQMAX];
   const int cw = static_cast<int>(blockDim.x) / kGroups;
@@ -257,7 +258,6 @@ __device__ __forceinline__ void reduce_cols(const float* __restrict__ ws, int G,
   // together, then summed in ascending block order.
   constexpr int kPer = kBwdMaxBlocks / kGroups;
   const int g0 = grp * G / kGroups, g1 = (grp + 1) * G / kGroups;
-  const int64_t bstride = static_cast<int64_t>(nparts) * h;
   for (int qb = q0; qb < q1; qb += cw) {   // block-uniform
     const int c4 = qb + cq;
     float4 sum[NP];
@@ -274,7 +274,7 @@ __device__ __forceinline__ void reduce_cols(const float* __restrict__ ws, int G,
         const int gi = g0 + i < G ? g0 + i : G - 1;
 #pragma unroll
         for (int j = 0; j < NP; ++j)
-          a[j][i] = reinterpret_cast<const float4*>(ws + gi * bstride + static_cast<int64_t>(j) * h)[cc];
+          a[j][i] = reinterpret_cast<const float4*>(ws + gi * bstride + j * sstride)[cc];
       }
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
@@ -318,13 +318,14 @@ struct ColOut {
 
 template <int NP>
 __global__ __launch_bounds__(kColQuads * kGroups) void sp_region_bwd_cols_kernel(const float* __restrict__ ws, int G,
-                                                                                 int h, int nparts, ColOut o) {
+                                                                                 int h, int64_t bstride,
+                                                                                 int64_t sstride, ColOut o) {
   const int nq = h / 4;
   const int q0 = blockIdx.x * kColQuads;
   float* out[NP];
 #pragma unroll
   for (int j = 0; j < NP; ++j) out[j] = o.p[j];
-  reduce_cols<kColQuads, NP>(ws, G, h, nparts, q0, q0 + kColQuads < nq ? q0 + kColQuads : nq, out);
+  reduce_cols<kColQuads, NP>(ws, G, bstride, sstride, q0, q0 + kColQuads < nq ? q0 + kColQuads : nq, out);
 }
 
 #ifndef SPR_BWD_MAX_THREADS
@@ -349,9 +350,9 @@ hipError_t launch_cols(const BwdParams& p, hipStream_t stream) {
   const int nq = p.h / 4;
   const dim3 grid((nq + kColQuads - 1) / kColQuads), block(kColQuads * kGroups);
   switch (np) {
-    case 1: hipLaunchKernelGGL(sp_region_bwd_cols_kernel<1>, grid, block, 0, stream, p.ws, p.G, p.h, p.nparts, o); break;
-    case 2: hipLaunchKernelGGL(sp_region_bwd_cols_kernel<2>, grid, block, 0, stream, p.ws, p.G, p.h, p.nparts, o); break;
-    default: hipLaunchKernelGGL(sp_region_bwd_cols_kernel<3>, grid, block, 0, stream, p.ws, p.G, p.h, p.nparts, o); break;
+    case 1: hipLaunchKernelGGL(sp_region_bwd_cols_kernel<1>, grid, block, 0, stream, p.ws, p.G, p.h, p.ws_bstride, p.ws_sstride, o); break;
+    case 2: hipLaunchKernelGGL(sp_region_bwd_cols_kernel<2>, grid, block, 0, stream, p.ws, p.G, p.h, p.ws_bstride, p.ws_sstride, o); break;
+    default: hipLaunchKernelGGL(sp_region_bwd_cols_kernel<3>, grid, block, 0, stream, p.ws, p.G, p.h, p.ws_bstride, p.ws_sstride, o); break;
   }
   return hipGetLastError();
 }
@@ -392,7 +393,10 @@ Shape bwd_shape(int h, int dtype) {
   return Shape{0, 0};
 }
 
-hipError_t launch_bwd(const BwdParams& p, int dtype, hipStream_t stream) {
+hipError_t launch_bwd(const BwdParams& params, int dtype, hipStream_t stream) {
+  BwdParams p = params;
+  p.ws_sstride = ws_slot_stride(p.h);
+  p.ws_bstride = ws_block_stride(p.h, p.nparts);
   if (p.G > 0) {
     const Shape sh = bwd_shape(p.h, dtype);
     const bool drop = p.dpartial != nullptr;

@@ -49,8 +49,10 @@ struct BwdParams {
   int32_t norm;
   int32_t G;
   // Partial slots per block: dgamma in slot 0, dbeta / dbias in slot_dbeta /
-  // slot_dbias (0: not computed).
+  // slot_dbias (0: not computed); strides in floats (set by launch_bwd).
   int32_t nparts;
+  int64_t ws_sstride;
+  int64_t ws_bstride;
   int32_t slot_dbeta;
   int32_t slot_dbias;
   // Dropout backward (dpartial != null): dpartial = dx * keep * scale and the
@@ -75,6 +77,21 @@ struct BwdParams {
 #endif
 constexpr int kBwdMaxBlocks = SPR_BWD_BLOCKS;
 inline int64_t bwd_blocks(int64_t T, int64_t /*h*/) { return T < kBwdMaxBlocks ? T : kBwdMaxBlocks; }
+
+// Workspace layout of the backward's partials (floats): slot j of block b at
+// b*ws_block_stride(h, nslots) + j*ws_slot_stride(h).  Both strides are 1 KiB
+// past a multiple of 2 KiB.  Every block writes its partial at the same
+// moment and stage 2 reads slot c of every block together; at power-of-two
+// strides those accesses are congruent modulo a large power of two and pile
+// onto the same HBM channels.
+#ifndef SPR_WS_PAD
+#define SPR_WS_PAD 1
+#endif
+inline int64_t ws_round(int64_t floats) {
+  return SPR_WS_PAD ? (floats + 511) / 512 * 512 + 256 : floats;
+}
+inline int64_t ws_slot_stride(int64_t h) { return ws_round(h); }
+inline int64_t ws_block_stride(int64_t h, int nslots) { return ws_round(nslots * ws_slot_stride(h)); }
 
 // Launchers: return hipSuccess or the launch error.  `dtype` 0 = f32, 1 = bf16.
 hipError_t launch_fwd(const FwdParams& p, int dtype, hipStream_t stream);

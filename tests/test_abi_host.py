@@ -71,8 +71,11 @@ def test_partials_stride_recommendation(lib):
 def test_workspace_bytes_is_pure(lib):
     ws = lib.sp_region_bwd_workspace_bytes
     assert ws(0, 8192) == 0 and ws(10, 0) == 0 and ws(-1, 8) == 0
-    assert ws(2048, 8192) == 256 * 2 * 8192 * 4       # one partial per block, 256 blocks
-    assert ws(64, 512) == 64 * 2 * 512 * 4            # T < 256: one row per block
+    # two slots per block at strides 1 KiB past a multiple of 2 KiB (floats: slot
+    # round_up(h, 512) + 256, block round_up(2 * slot, 512) + 256), 256 blocks
+    assert ws(2048, 8192) == 256 * (2 * (8192 + 256) + 256) * 4
+    assert ws(64, 512) == 64 * (2 * (512 + 256) + 256) * 4        # T < 256: one row per block
+    assert ws(10, 520) == 10 * (2560 + 256) * 4                  # slot 1024 + 256 floats; 2 slots 2560 -> + 256
     assert ws(16384, 8192) == ws(2048, 8192)
 
 
@@ -135,9 +138,15 @@ def test_fwd_empty_shard_is_noop(lib):
     assert call_fwd(lib, a) == spr.SPR_OK
 
 
+# Workspace bytes of the T = 64, h = 512 backward cases: 64 blocks, slots of
+# 512 + 256 floats, blocks of round_up(nslots * 768, 512) + 256 floats.
+WS2 = 64 * (1536 + 256) * 4
+WS3 = 64 * (2560 + 256) * 4
+
+
 def bwd_args(**over):
     a = dict(b=1, s=256, h=512, t=4, gamma=P, norm=0, dtype=0, dy=P, z=P, mean=P, rstd=P, dres=None, dx=P,
-             dgamma=P, dbeta=P, ws=P, ws_bytes=64 * 2 * 512 * 4, stream=None)
+             dgamma=P, dbeta=P, ws=P, ws_bytes=WS2, stream=None)
     a.update(over)
     return a
 
@@ -149,7 +158,7 @@ def call_bwd(lib, a):
 
 
 BWD_CASES = [
-    (dict(ws_bytes=64 * 2 * 512 * 4 - 1), INVALID), (dict(ws=None), INVALID),
+    (dict(ws_bytes=WS2 - 1), INVALID), (dict(ws=None), INVALID),
     (dict(dy=None), INVALID), (dict(z=None), INVALID), (dict(rstd=None), INVALID), (dict(dx=None), INVALID),
     (dict(dgamma=None), INVALID), (dict(gamma=None), INVALID), (dict(mean=None), INVALID),
     (dict(norm=1, dbeta=P, mean=None), INVALID), (dict(norm=1, mean=P, dbeta=None), INVALID),
@@ -164,7 +173,7 @@ def test_bwd_rejects(lib, over, status):
 
 
 def bwd_dropout_args(**over):
-    a = dict(bwd_args(ws_bytes=64 * 3 * 512 * 4), p=0.1, rank=1, seed=7, cu=None, nseq=0, dpartial=P, dbias=P)
+    a = dict(bwd_args(ws_bytes=WS3), p=0.1, rank=1, seed=7, cu=None, nseq=0, dpartial=P, dbias=P)
     a.update(over)
     return a
 
@@ -177,8 +186,8 @@ def call_bwd_dropout(lib, a):
 
 
 BWD_DROPOUT_CASES = BWD_CASES[2:] + [
-    (dict(ws_bytes=64 * 3 * 512 * 4 - 1), INVALID),          # three partial slots per block
-    (dict(ws_bytes=64 * 2 * 512 * 4), INVALID),
+    (dict(ws_bytes=WS3 - 1), INVALID),          # three partial slots per block
+    (dict(ws_bytes=WS2), INVALID),
     (dict(ws=None), INVALID),
     (dict(dpartial=None), INVALID),
     (dict(p=1.0), INVALID), (dict(p=-0.1), INVALID), (dict(p=float("nan")), INVALID),
@@ -197,7 +206,10 @@ def test_bwd_dropout_workspace_bytes(lib):
     ws3, ws2 = lib.sp_region_bwd_dropout_workspace_bytes, lib.sp_region_bwd_workspace_bytes
     assert ws3(0, 64) == 0 and ws3(5, 0) == 0
     for T, h in [(64, 512), (2048, 8192), (100000, 5120), (1, 8)]:
-        assert ws3(T, h) * 2 == ws2(T, h) * 3
+        slot = (h + 511) // 512 * 512 + 256
+        blocks = min(T, 256)
+        assert ws2(T, h) == blocks * ((2 * slot + 511) // 512 * 512 + 256) * 4
+        assert ws3(T, h) == blocks * ((3 * slot + 511) // 512 * 512 + 256) * 4
 
 
 def test_bwd_dropout_empty_shard_needs_no_outputs(lib):
