@@ -188,17 +188,17 @@ def run(args):
     cu = torch.tensor(inp["cu_seqlens"], dtype=torch.int32, device=dev) if inp["cu_seqlens"] is not None else None
 
     def step(i, ev=None):
+        # ev: four events; each region call stamps its first kernel's start and
+        # last kernel's end into a pair of them from the dispatch packets.
         s = sets[i % len(sets)]
         if ev is not None:
-            ev[0].record()
+            spr.time_next_call(ev[0], ev[1])
         fo = spr.fwd(s["P"], gamma, beta, bias=bias, residual=s["res"], b=inp["b"], s=inp["s"], t=w.t, rank=0,
                      eps=w.eps, p_drop=w.p_drop, seed=inp["seed"], norm=w.norm, cu_seqlens=cu, out=s["fo"])
         if ev is not None:
-            ev[1].record()
+            spr.time_next_call(ev[2], ev[3])
         spr.bwd(s["dy"], fo.z, fo.mean, fo.rstd, gamma, b=inp["b"], s=inp["s"], t=w.t, norm=w.norm,
                 workspace=ws, out=s["bo"])
-        if ev is not None:
-            ev[2].record()
 
     # Copy-kernel ceiling on 1 GiB (also the reference for the traffic counters).
     nb = 1 << 30
@@ -223,9 +223,8 @@ def run(args):
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: exactly K steps, nothing else on the stream.  (A timing
-    # event costs the GPU a few microseconds at every record, so the per-launch
-    # events go in the second, otherwise identical, pass below.)
+    # Timed region: exactly K steps, nothing else on the stream.  (Kernel
+    # durations come from the second, otherwise identical, pass below.)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -233,9 +232,14 @@ def run(args):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # Kernel durations: the same K steps with events around every launch, on
-    # the stream the library launches on (torch's current stream).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Kernel durations: the same K steps, every region call stamping HIP
+    # events from its kernels' own dispatch packets (sp_region_time_next_call:
+    # no marker packets, which cost the GPU ~3 us each, on the stream the
+    # library launches on).  Each event is recorded once first so it exists.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs:
+        for x in e:
+            x.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for i in range(args.steps):
@@ -252,26 +256,28 @@ def run(args):
         douts.append(spr.BwdDropoutOut(bo.dx, torch.empty_like(bo.dx), bo.dgamma, bo.dbeta,
                                        torch.empty(h, device=dev) if w.has_bias else None))
     evd = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in evd:
+        for x in e:
+            x.record()
     for i in range(args.steps):
         s, fo = sets[i % len(sets)], sets[i % len(sets)]["fo"]
-        evd[i][0].record()
+        spr.time_next_call(evd[i][0], evd[i][1])
         spr.bwd_dropout(s["dy"], fo.z, fo.mean, fo.rstd, gamma, b=inp["b"], s=inp["s"], t=w.t, rank=0,
                         p_drop=w.p_drop, seed=inp["seed"], norm=w.norm, cu_seqlens=cu, workspace=ws_d,
                         want_dbias=w.has_bias, out=douts[i % len(sets)])
-        evd[i][1].record()
     torch.cuda.synchronize()
     bwd_dropout_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evd]) * 1e3)
     del douts, ws_d
 
     fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
     fb, bb = fwd_bytes(w, T), bwd_bytes(w, T)
     fwd_s = float(fwd_ms.mean()) * 1e-3
     achieved = fb / fwd_s / 1e9
     step_ms = elapsed / args.steps * 1e3
     eprint(f"[bench] fwd {fwd_ms.mean() * 1e3:.1f} us (p50 {np.median(fwd_ms) * 1e3:.1f}), "
            f"bwd {bwd_ms.mean() * 1e3:.1f} us, step {step_ms * 1e3:.1f} us wall "
-           f"({elapsed_ev / args.steps * 1e6:.1f} with events); fwd {achieved:.0f} GB/s, "
+           f"({elapsed_ev / args.steps * 1e6:.1f} in the timestamped pass); fwd {achieved:.0f} GB/s, "
            f"fwd+bwd {(fb + bb) / ((fwd_ms.mean() + bwd_ms.mean()) * 1e-3) / 1e9:.0f} GB/s")
 
     plan = plan_timing(W)
@@ -294,7 +300,7 @@ def run(args):
         "config": {"workload": w.name, "s": inp["s"], "b": inp["b"], "h": h, "t": w.t, "local_tokens": T,
                    "p_drop": w.p_drop, "norm": w.norm, "rank": 0, "rotating_sets": args.sets,
                    "slabs": args.slabs, "slab_stride": stride},
-        "step_us_with_events": elapsed_ev / args.steps * 1e6,
+        "step_us_timestamped_pass": elapsed_ev / args.steps * 1e6,
         "fwd_us": float(fwd_ms.mean() * 1e3),
         "bwd_us": float(bwd_ms.mean() * 1e3),
         "fwd_bwd_hbm_gbs": (fb + bb) / (kernel_us * 1e-6) / 1e9,

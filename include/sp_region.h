@@ -75,6 +75,18 @@ const char* sp_region_strerror(int status);
 int sp_region_last_hip_error(void);
 
 /*
+ * Profiling hook.  The next sp_region_fwd, sp_region_bwd or
+ * sp_region_bwd_dropout call on this thread records start_event when its
+ * first kernel starts and stop_event when its last kernel ends: timestamps
+ * carried by the kernels' own dispatch packets (hipExtLaunchKernel), so no
+ * extra packets are placed on the stream.  The events are hipEvent_t passed
+ * as void*, created by the caller with timing enabled.  The hook applies to
+ * exactly one call (whatever its status) and is then cleared; both NULL clears
+ * it.  Returns SPR_ERR_INVALID_ARG if exactly one of them is NULL.
+ */
+int sp_region_time_next_call(void* start_event, void* stop_event);
+
+/*
  * Recommended slab_stride, in elements, for the forward's t partial slabs of
  * T = n_local_tokens rows of h channels of `dtype`: the smallest stride
  * >= T*h whose size in bytes is 1 KiB more than a multiple of 2 KiB.  The

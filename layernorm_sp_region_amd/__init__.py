@@ -34,6 +34,7 @@ SIGNATURES = {
     "sp_region_abi_version": (ctypes.c_int, []),
     "sp_region_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "sp_region_last_hip_error": (ctypes.c_int, []),
+    "sp_region_time_next_call": (ctypes.c_int, [_VP, _VP]),
     "sp_region_fwd": (ctypes.c_int, [_I64, _I64, _I64, _I32, _F32, _F32, _VP, _VP, _I32, _I32, _I32, _U64,
                                      _VP, _I64, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
     "sp_region_partials_stride": (_I64, [_I64, _I64, _I32]),
@@ -192,6 +193,15 @@ def fwd(partials, gamma, beta=None, *, bias=None, residual=None, b: int, s: int,
                            _ptr(mask), stream)
     _check("sp_region_fwd", st)
     return FwdOut(z, y, mean, rstd, mask)
+
+
+def time_next_call(start, stop) -> None:
+    """The next region call on this thread stamps its first kernel's start
+    into `start` and its last kernel's end into `stop` (torch.cuda.Event
+    objects with timing enabled, already recorded once so that they exist)."""
+    h0 = start.cuda_event if start is not None else None
+    h1 = stop.cuda_event if stop is not None else None
+    _check("sp_region_time_next_call", load_library().sp_region_time_next_call(h0, h1))
 
 
 def partials_stride(T: int, h: int, dtype) -> int:

@@ -7,9 +7,18 @@
 #include "sp_region.h"
 #include "spr_internal.h"
 
+namespace spr {
+thread_local LaunchEvents g_launch_events = {nullptr, nullptr};
+}  // namespace spr
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// The hook applies to one region call; cleared on every exit path.
+struct ClearLaunchEvents {
+  ~ClearLaunchEvents() { spr::g_launch_events = {nullptr, nullptr}; }
+};
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned16_or_null(const void* p) { return p == nullptr || aligned16(p); }
@@ -56,6 +65,12 @@ const char* sp_region_strerror(int status) {
 
 int sp_region_last_hip_error(void) { return g_last_hip_error; }
 
+int sp_region_time_next_call(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return SPR_ERR_INVALID_ARG;
+  spr::g_launch_events = {static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+  return SPR_OK;
+}
+
 int sp_region_fwd(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p_drop,
                   const void* gamma, const void* beta,
                   int32_t norm, int32_t dtype, int32_t rank, uint64_t seed,
@@ -65,6 +80,7 @@ int sp_region_fwd(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p
                   void* z, void* y, float* mean, float* rstd,
                   uint8_t* mask_out,
                   void* stream) {
+  ClearLaunchEvents clear_hook;
   int64_t T = 0;
   int st = check_shape(b, s, h, t, norm, dtype, &T);
   if (st != SPR_OK) return st;
@@ -193,6 +209,7 @@ int sp_region_bwd(int64_t b, int64_t s, int64_t h, int32_t t,
                   void* dx, float* dgamma, float* dbeta,
                   void* workspace, size_t workspace_bytes,
                   void* stream) {
+  ClearLaunchEvents clear_hook;
   spr::BwdParams p;
   const int st = prepare_bwd(b, s, h, t, gamma, norm, dtype, dy, z, mean, rstd, dres_in, dx, dgamma, dbeta,
                              workspace, workspace_bytes, false, &p);
@@ -209,6 +226,7 @@ int sp_region_bwd_dropout(int64_t b, int64_t s, int64_t h, int32_t t,
                           void* dx, void* dpartial, float* dgamma, float* dbeta, float* dbias,
                           void* workspace, size_t workspace_bytes,
                           void* stream) {
+  ClearLaunchEvents clear_hook;
   spr::BwdParams p;
   const int st = prepare_bwd(b, s, h, t, gamma, norm, dtype, dy, z, mean, rstd, dres_in, dx, dgamma, dbeta,
                              workspace, workspace_bytes, true, &p);

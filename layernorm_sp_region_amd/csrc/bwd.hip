@@ -349,10 +349,12 @@ hipError_t launch_cols(const BwdParams& p, hipStream_t stream) {
   if (p.slot_dbias > 0) o.p[np++] = p.dbias;
   const int nq = p.h / 4;
   const dim3 grid((nq + kColQuads - 1) / kColQuads), block(kColQuads * kGroups);
+  const KernelRole role = p.G > 0 ? KernelRole::kLast : KernelRole::kOnly;
+  const float* ws = p.ws;
   switch (np) {
-    case 1: hipLaunchKernelGGL(sp_region_bwd_cols_kernel<1>, grid, block, 0, stream, p.ws, p.G, p.h, p.ws_bstride, p.ws_sstride, o); break;
-    case 2: hipLaunchKernelGGL(sp_region_bwd_cols_kernel<2>, grid, block, 0, stream, p.ws, p.G, p.h, p.ws_bstride, p.ws_sstride, o); break;
-    default: hipLaunchKernelGGL(sp_region_bwd_cols_kernel<3>, grid, block, 0, stream, p.ws, p.G, p.h, p.ws_bstride, p.ws_sstride, o); break;
+    case 1: launch_kernel(sp_region_bwd_cols_kernel<1>, grid, block, stream, role, ws, p.G, p.h, p.ws_bstride, p.ws_sstride, o); break;
+    case 2: launch_kernel(sp_region_bwd_cols_kernel<2>, grid, block, stream, role, ws, p.G, p.h, p.ws_bstride, p.ws_sstride, o); break;
+    default: launch_kernel(sp_region_bwd_cols_kernel<3>, grid, block, stream, role, ws, p.G, p.h, p.ws_bstride, p.ws_sstride, o); break;
   }
   return hipGetLastError();
 }
@@ -362,7 +364,7 @@ hipError_t launch_stages(const BwdParams& p, const Shape& sh, hipStream_t stream
   constexpr int MAXBS = SPR_BWD_MAX_THREADS;
   constexpr int RING = ring_for<VPT, MAXBS, DROP>();
   const dim3 grid(static_cast<unsigned>(p.G)), block(sh.threads);
-  hipLaunchKernelGGL((sp_region_bwd_rows_kernel<E, VPT, RING, DRES, DROP, MAXBS>), grid, block, 0, stream, p);
+  launch_kernel(sp_region_bwd_rows_kernel<E, VPT, RING, DRES, DROP, MAXBS>, grid, block, stream, KernelRole::kFirst, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_cols(p, stream);

@@ -300,8 +300,8 @@ hipError_t launch_ns(const FwdParams& p, hipStream_t stream) {
   switch (p.t) {
 #define SPR_NS(N)                                                                                          \
   case N:                                                                                                  \
-    if (mask) hipLaunchKernelGGL((sp_region_fwd_kernel<E, N, VPL, WPR, true>), grid, block, 0, stream, p); \
-    else hipLaunchKernelGGL((sp_region_fwd_kernel<E, N, VPL, WPR, false>), grid, block, 0, stream, p);     \
+    if (mask) launch_kernel(sp_region_fwd_kernel<E, N, VPL, WPR, true>, grid, block, stream, KernelRole::kOnly, p); \
+    else launch_kernel(sp_region_fwd_kernel<E, N, VPL, WPR, false>, grid, block, stream, KernelRole::kOnly, p);     \
     break;
     SPR_NS(1) SPR_NS(2) SPR_NS(3) SPR_NS(4) SPR_NS(5) SPR_NS(6) SPR_NS(7) SPR_NS(8)
 #undef SPR_NS

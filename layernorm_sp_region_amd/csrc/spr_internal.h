@@ -1,10 +1,31 @@
 // Host-side contract between the C ABI (abi.cpp) and the kernel TUs.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace spr {
+
+// Profiling hook (sp_region_time_next_call): events the next region call on
+// this thread stamps from its kernels' dispatch packets -- start at its first
+// kernel, stop at its last.  Cleared by the ABI layer after each call.
+struct LaunchEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+extern thread_local LaunchEvents g_launch_events;
+
+enum class KernelRole { kOnly, kFirst, kLast };
+
+// Every region kernel is launched through here: hipExtLaunchKernelGGL with
+// the hook's events (none when the hook is clear).
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t stream, KernelRole role, Args... args) {
+  hipEvent_t start = role != KernelRole::kLast ? g_launch_events.start : nullptr;
+  hipEvent_t stop = role != KernelRole::kFirst ? g_launch_events.stop : nullptr;
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, args...);
+}
 
 // Parameters of one forward launch (validated by the ABI layer).
 struct FwdParams {

@@ -212,6 +212,31 @@ def test_bitwise_reproducible(cuda_device):
         assert np.array_equal(a[k], b[k]), k
 
 
+def test_time_next_call_stamps_one_call(cuda_device):
+    """The profiling hook stamps the next region call's kernel start/end from
+    the dispatch packets and then clears itself: a later call leaves the
+    events alone."""
+    import torch
+    w = W.BY_NAME["page_demo"]
+    inp = inputs_for(w)
+    t = lambda a: W.as_torch(a, cuda_device)
+    P, g, be, res = t(inp["partials"]), t(inp["gamma"]), t(inp["beta"]), t(inp["residual"])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in ev:
+        e.record()
+    kw = dict(b=inp["b"], s=inp["s"], t=w.t, rank=0, eps=w.eps, p_drop=w.p_drop, seed=inp["seed"], norm=w.norm)
+    spr.time_next_call(ev[0], ev[1])
+    spr.fwd(P, g, be, residual=res, **kw)
+    torch.cuda.synchronize()
+    first = ev[0].elapsed_time(ev[1])
+    assert 0.0 < first < 50.0, first             # one forward of a 512-row shard: microseconds
+    spr.fwd(P, g, be, residual=res, **kw)        # hook cleared: events keep their stamps
+    torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) == first
+    with pytest.raises(spr.SpRegionError):
+        spr.time_next_call(ev[0], None)
+
+
 def test_ranks_tile_unsharded_mask(cuda_device):
     """On the GPU, per-rank masks of a uniform shard tile the t = 1 mask of the
     whole sequence (same seed, global token index)."""
