@@ -174,8 +174,8 @@ EDGE = [
               bias=False, residual=False), 5, {}),
     # padded slab stride and an extra residual-stream gradient
     (W.custom("padded_slabs_dres", h=256, t=4, s=4 * 33, p_drop=0.2), 1, dict(padded=5, dres=True)),
-    # 257 vectors per row: 6 slots per lane of LDS-resident z, most lanes of the last slot clamped
-    (W.custom("h2056_6slots", h=2056, t=2, s=2 * 40, p_drop=0.15), 1, {}),
+    # 257 vectors per row: 8 slots per lane of LDS-resident z, all but one vector of the last 4 clamped
+    (W.custom("h2056_257vec", h=2056, t=2, s=2 * 40, p_drop=0.15), 1, {}),
     # t = 6, h = 5120 (the ragged workload's width) uniform, LayerNorm without beta
     (W.custom("t6_h5120_nobeta", h=5120, t=6, s=6 * 20, p_drop=0.1, beta=False), 3, {}),
 ]
