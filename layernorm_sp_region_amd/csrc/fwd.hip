@@ -318,6 +318,9 @@ hipError_t launch_e(const FwdParams& p, const Shape& sh, hipStream_t stream) {
       case 2: return launch_ns<E, 2, 1>(p, stream);
       case 4: return launch_ns<E, 4, 1>(p, stream);
       case 8: return launch_ns<E, 8, 1>(p, stream);
+      case 10: return launch_ns<E, 10, 1>(p, stream);
+      case 12: return launch_ns<E, 12, 1>(p, stream);
+      case 14: return launch_ns<E, 14, 1>(p, stream);
       case 16: return launch_ns<E, 16, 1>(p, stream);
       default: return hipErrorInvalidValue;
     }
@@ -329,14 +332,14 @@ hipError_t launch_e(const FwdParams& p, const Shape& sh, hipStream_t stream) {
 }  // namespace
 
 // Waves per row and vectors per lane: rows of up to 1024 vectors (h <= 8192
-// bf16, 4096 f32) get one wave and the smallest power-of-two VPL covering
-// them; wider rows (up to 2048 vectors) get two waves of 16.  Shape.threads
-// is 64 * waves per row.  (h = 8192 bf16 -> 1 x 16; h = 5120 -> 1 x 16 with
-// 6 slots clamped; h = 512 f32 -> 1 x 2; h = 16384 bf16 -> 2 x 16.)
+// bf16, 4096 f32) get one wave and the smallest VPL in {1, 2, 4, 8, 10, 12,
+// 14, 16} covering them; wider rows (up to 2048 vectors) get two waves of 16.
+// Shape.threads is 64 * waves per row.  (h = 8192 bf16 -> 1 x 16; h = 5120
+// -> 1 x 10; h = 512 f32 -> 1 x 2; h = 16384 bf16 -> 2 x 16.)
 Shape fwd_shape(int h, int dtype) {
   const int vec = dtype == 1 ? 8 : 4;
   const int nvec = h / vec;
-  for (int vpl : {1, 2, 4, 8, 16})
+  for (int vpl : {1, 2, 4, 8, 10, 12, 14, 16})
     if (nvec <= 64 * vpl) return Shape{vpl, 64};
   if (nvec <= 2 * 64 * 16) return Shape{16, 128};
   return Shape{0, 0};
