@@ -20,6 +20,7 @@ import argparse
 import csv
 import glob
 import hashlib
+import re
 import json
 import os
 import sys
@@ -61,11 +62,25 @@ def bwd_dropout_bytes(w, T):
     return bwd_bytes(w, T) + T * w.h * w.elem_bytes + w.h * 4
 
 
-def kernel_source_hash():
+def code_text(src: str) -> str:
+    """C++ source without comments and with whitespace collapsed: what the
+    compiler sees (the kernel sources hold no string literals with // or /*)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def kernel_source_hash(read=None):
+    """Hash of the forward kernel's code (comments and layout ignored), the
+    key under which the committed traffic counters are valid."""
     h = hashlib.sha256()
     for p in FWD_KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+                text = f.read()
+        else:
+            text = read(p)
+        h.update(code_text(text).encode())
     return h.hexdigest()[:16]
 
 

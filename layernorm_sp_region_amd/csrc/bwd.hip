@@ -6,15 +6,19 @@
 //   plus dres_in (the gradient reaching z through the residual stream);
 //   dgamma_j = sum_i dy_ij*xhat_ij,  dbeta_j = sum_i dy_ij over the T rows.
 //
+// Through the dropout and the slab sum (the DROP variant, row-linear side of
+// the same section): dpartial = dx * keep * scale with the forward's own
+// mask, the gradient of every slab, and dbias_j = sum_i dpartial_ij.
+//
 // Stage 1 (sp_region_bwd_rows_kernel): G blocks, block b owns the contiguous
 // rows [b*T/G, (b+1)*T/G).  Each thread owns a fixed set of columns, keeps
-// their gamma and their dgamma/dbeta running sums in registers across rows,
-// and the block writes one [2][h] float32 partial to the workspace.  Rows
-// stream through a ring of RING packed row buffers (RING rows in flight per
-// block); each row's two sums take one block reduction.
+// their gamma and their dgamma/dbeta (/dbias) running sums in registers
+// across rows, and the block writes one float32 partial per gradient to the
+// workspace.  Rows stream through a ring of RING packed row buffers (RING
+// rows in flight per block); each row's two sums take one block reduction.
 //
-// Stage 2 (sp_region_bwd_cols_kernel): dgamma/dbeta = the G partials summed in
-// ascending block order, split over 32 groups whose sums are combined in
+// Stage 2 (sp_region_bwd_cols_kernel): each gradient = the G partials summed
+// in ascending block order, split over 32 groups whose sums are combined in
 // group order -- a fixed tree, so results are bitwise reproducible.
 
 #include "spr_device.h"

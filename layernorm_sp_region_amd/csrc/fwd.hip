@@ -5,7 +5,7 @@
 //   acc = acc + bias                      if bias
 //   d   = keep ? acc * scale : 0          if p > 0 (Philox-4x32-10 keep bit)
 //   z   = round(residual + d)             stored; statistics use the rounded z
-//   LayerNorm: mean, population variance (two passes over registers),
+//   LayerNorm: mean, population variance (second pass over the packed z),
 //              y = (z - mean) * rstd * gamma + beta
 //   RMSNorm:   y = z * rstd * gamma, rstd = 1/sqrt(mean(z^2) + eps)
 //
@@ -14,17 +14,19 @@
 // exactly; the normalisation uses explicit fmaf.
 //
 // Memory plan.  Lane l of wave w of the row owns the 16-byte vectors
-// v = l + 64*(w + WPR*k), k < VPL, so every load instruction of a wave reads
-// 1 KB of contiguous row.  The row is streamed in chunks of C vectors per
-// lane: the t slab vectors and the residual vector of chunk c+1 are in
-// flight while chunk c is summed, masked and stored, and the rounded z stays
-// packed in registers (h*2/(64*WPR) bytes per lane in bf16).  Statistics are
-// wave butterflies, combined through LDS when WPR > 1 (one row per block, so
-// a barrier only couples the row's own waves).  With WPR = 1 waves never
-// wait for each other; WPR = 2 halves the registers per wave, doubling the
-// waves per SIMD that hide the dropout hash and conversions behind HBM.
-// Slabs and residual are streamed with a nontemporal hint; gamma, beta and
-// bias (read by every row) use ordinary cached loads.
+// v = l + 64*(w + WPR*k), k < VPL (VPL slots per lane), so every load
+// instruction of a wave reads 1 KB of contiguous row.  The row is streamed
+// one slot at a time: the t slab vectors, the residual and the bias of slot
+// k+1 are in flight while slot k is summed, masked, rounded and stored.  The
+// rounded z stays packed -- in LDS for rows of 8-16 slots per lane (each lane
+// reads back only what it wrote, so no barrier), in registers for shorter
+// rows -- for the statistics (a second pass) and the y phase, which fetches
+// gamma/beta one slot ahead.  Wave sums use DPP row steps plus readlane;
+// two-wave rows (WPR = 2, h above 8192 bf16) combine their two sums through
+// LDS in wave order.  Every memory instruction is unconditional (see the
+// kernel), and row base pointers are wave-uniform (SGPR + 32-bit lane
+// offsets).  Slabs and residual use nontemporal loads; gamma, beta and bias
+// (read by every row) ordinary cached loads.
 #include "spr_device.h"
 #include "spr_internal.h"
 
