@@ -281,3 +281,36 @@ def test_oracle_philox_matches_rocrand_host_generator(cuda_device):
     mine = np.stack(words, axis=-1).reshape(-1)
     log(f"  rocrand first words {[hex(x) for x in outb[:4]]}, oracle {[hex(x) for x in mine[:4]]}")
     assert np.array_equal(outb, mine)
+
+
+# Every forward slot count (1, 2, 4, 8, 10, 12, 14, 16 vectors per lane, and
+# two waves per row) in both dtypes, against the oracle, with ragged and
+# uniform shards, both norms, with and without dropout/bias/residual.
+SLOT_SHAPES = [
+    # (h, dtype, norm, t, T-or-lengths, p, bias, residual)
+    (64, "bf16", "layernorm", 3, 21, 0.3, True, True),           # 8 vectors: 1 slot
+    (1032, "bf16", "rmsnorm", 2, 17, 0.0, False, True),          # 129 vectors: 4 slots
+    (4104, "bf16", "layernorm", 4, (12, 0, 20), 0.2, True, False),   # 513 vectors: 10 slots, ragged
+    (6144, "bf16", "layernorm", 5, 9, 0.1, True, True),          # 768 vectors: 12 slots
+    (7168, "bf16", "rmsnorm", 7, 6, 0.25, False, True),          # 896 vectors: 14 slots
+    (8200, "bf16", "layernorm", 2, 5, 0.1, True, True),          # 1025 vectors: two waves per row
+    (2560, "f32", "layernorm", 3, 8, 0.15, True, True),          # 640 vectors: 10 slots
+    (3072, "f32", "rmsnorm", 4, (8, 4), 0.4, False, True),       # 768 vectors: 12 slots, ragged
+    (3584, "f32", "layernorm", 2, 7, 0.0, True, False),          # 896 vectors: 14 slots
+    (4100, "f32", "layernorm", 1, 5, 0.2, False, True),          # 1025 vectors: two waves per row
+]
+
+
+@pytest.mark.parametrize("shape", SLOT_SHAPES, ids=[f"h{s[0]}_{s[1]}_{s[2]}_t{s[3]}" for s in SLOT_SHAPES])
+def test_every_slot_count(cuda_device, shape):
+    h, dtype, norm, t, rows, p, bias, res = shape
+    if isinstance(rows, tuple):
+        w = W.custom(f"slots_h{h}", h=h, t=t, dtype=dtype, norm=norm, p_drop=p, bias=bias, residual=res,
+                     lengths=tuple(t * r for r in rows))
+    else:
+        w = W.custom(f"slots_h{h}", h=h, t=t, dtype=dtype, norm=norm, p_drop=p, bias=bias, residual=res, s=t * rows)
+    rank = t - 1
+    log(f"[parity-slots] h={h} {dtype} {norm} t={t} rows={rows} p={p} rank={rank}")
+    inp = W.make_inputs(w)
+    gpu = run_gpu(inp, w, rank, cuda_device, recommended_stride=True)
+    compare(w, inp, gpu, rank)
