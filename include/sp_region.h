@@ -148,6 +148,26 @@ int sp_region_fwd(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p
                   void* stream);
 
 /*
+ * sp_region_fwd with the t partial slabs given as a HOST array slabs[0..t) of
+ * device pointers, each to a row-major [T][h] slab, 16-byte aligned: the
+ * slabs may live in separate buffers (receive buffers of a reduce-scatter,
+ * say) or, peer-mapped, in other GPUs' memory -- each is read through its own
+ * base address, in the same order and with the same results as the strided
+ * form.  The array is read during the call only.  Every other argument,
+ * check and result as in sp_region_fwd; a NULL array or slab pointer returns
+ * SPR_ERR_INVALID_ARG, a misaligned slab SPR_ERR_ALIGNMENT.
+ */
+int sp_region_fwd_slabs(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p_drop,
+                        const void* gamma, const void* beta,
+                        int32_t norm, int32_t dtype, int32_t rank, uint64_t seed,
+                        const void* const* slabs,
+                        const void* bias, const void* residual,
+                        const int32_t* cu_seqlens, int32_t nseq,
+                        void* z, void* y, float* mean, float* rstd,
+                        uint8_t* mask_out,
+                        void* stream);
+
+/*
  * Bytes of device workspace sp_region_bwd needs for n_local_tokens = T rows of
  * h channels: float32 dgamma/dbeta partial sums of G = min(T, 256) row blocks,
  * two slots of h per block.  Slots and blocks sit at strides 1 KiB past a

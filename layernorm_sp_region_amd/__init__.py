@@ -38,6 +38,8 @@ SIGNATURES = {
     "sp_region_fwd": (ctypes.c_int, [_I64, _I64, _I64, _I32, _F32, _F32, _VP, _VP, _I32, _I32, _I32, _U64,
                                      _VP, _I64, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
     "sp_region_partials_stride": (_I64, [_I64, _I64, _I32]),
+    "sp_region_fwd_slabs": (ctypes.c_int, [_I64, _I64, _I64, _I32, _F32, _F32, _VP, _VP, _I32, _I32, _I32, _U64,
+                                           _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
     "sp_region_bwd_workspace_bytes": (_SZ, [_I64, _I64]),
     "sp_region_bwd": (ctypes.c_int, [_I64, _I64, _I64, _I32, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
                                      _VP, _VP, _VP, _VP, _SZ, _VP]),
@@ -144,7 +146,9 @@ def fwd(partials, gamma, beta=None, *, bias=None, residual=None, b: int, s: int,
     """Forward of the region.
 
     partials: [t][T][h] tensor (slab k = partials[k]; each slab row-major; the
-    slab stride may exceed T*h).  cu_seqlens: None (uniform shard) or the
+    slab stride may exceed T*h), or a list of t separate [T][h] tensors
+    (sp_region_fwd_slabs: slab k read through its own pointer, wherever it
+    lives).  cu_seqlens: None (uniform shard) or the
     host list / CPU tensor / int32 CUDA tensor of local row offsets of a packed
     batch (b must be 1; a CUDA tensor is trusted as-is).  `out` may supply
     preallocated outputs.  Returns FwdOut(z, y, mean, rstd, mask).
@@ -152,21 +156,34 @@ def fwd(partials, gamma, beta=None, *, bias=None, residual=None, b: int, s: int,
     import torch
     lib = load_library()
     nc = _norm_code(norm)
-    dev = partials.device
-    dt = partials.dtype
+    slab_list = None
+    if isinstance(partials, (list, tuple)):
+        slab_list = list(partials)
+        if len(slab_list) != t or t < 1:
+            raise ValueError(f"expected {t} slab tensors, got {len(slab_list)}")
+        first = slab_list[0]
+        dev, dt = first.device, first.dtype
+        if first.dim() != 2:
+            raise ValueError("each slab must be [T][h]")
+        T, h = first.shape
+        for k, sk in enumerate(slab_list):
+            _require(sk, f"slab {k}", dev, dt, (T, h))
+    else:
+        dev = partials.device
+        dt = partials.dtype
+        if partials.dim() != 3 or partials.shape[0] != t:
+            raise ValueError(f"partials must be [t={t}][T][h], got {tuple(partials.shape)}")
+        _, T, h = partials.shape
+        if not partials.is_cuda:
+            raise ValueError("partials must be a CUDA tensor")
+        # Strides of size-0/1 dims carry no layout information (numpy gives an
+        # inserted axis stride 0), so only meaningful ones are checked.
+        if T > 0 and ((h > 1 and partials.stride(2) != 1) or (T > 1 and partials.stride(1) != h)):
+            raise ValueError("each slab of partials must be row-major contiguous")
+        slab_stride = partials.stride(0) if t > 1 else T * h
     dcode = _dtype_code(dt)
-    if partials.dim() != 3 or partials.shape[0] != t:
-        raise ValueError(f"partials must be [t={t}][T][h], got {tuple(partials.shape)}")
-    _, T, h = partials.shape
     if T != local_tokens(b, s, t):
         raise ValueError(f"partials hold {T} rows, expected b*s/t = {local_tokens(b, s, t)}")
-    if not partials.is_cuda or partials.device != dev:
-        raise ValueError("partials must be a CUDA tensor")
-    # Strides of size-0/1 dims carry no layout information (numpy gives an
-    # inserted axis stride 0), so only meaningful ones are checked.
-    if T > 0 and ((h > 1 and partials.stride(2) != 1) or (T > 1 and partials.stride(1) != h)):
-        raise ValueError("each slab of partials must be row-major contiguous")
-    slab_stride = partials.stride(0) if t > 1 else T * h
     _require(gamma, "gamma", dev, dt, (h,))
     _require(beta, "beta", dev, dt, (h,))
     _require(bias, "bias", dev, dt, (h,))
@@ -187,6 +204,14 @@ def fwd(partials, gamma, beta=None, *, bias=None, residual=None, b: int, s: int,
         _require(rstd, "rstd", dev, torch.float32, (T,))
         _require(mask, "mask", dev, torch.uint8, (T, h))
     stream = torch.cuda.current_stream(dev).cuda_stream
+    if slab_list is not None:
+        table = (ctypes.c_void_p * t)(*[sk.data_ptr() for sk in slab_list])
+        st = lib.sp_region_fwd_slabs(b, s, h, t, float(eps), float(p_drop), _ptr(gamma), _ptr(beta), nc, dcode,
+                                     rank, int(seed) & 0xFFFFFFFFFFFFFFFF, table, _ptr(bias), _ptr(residual),
+                                     _ptr(cu_dev), nseq, _ptr(z), _ptr(y), _ptr(mean), _ptr(rstd), _ptr(mask),
+                                     stream)
+        _check("sp_region_fwd_slabs", st)
+        return FwdOut(z, y, mean, rstd, mask)
     st = lib.sp_region_fwd(b, s, h, t, float(eps), float(p_drop), _ptr(gamma), _ptr(beta), nc, dcode, rank,
                            int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(partials), slab_stride, _ptr(bias),
                            _ptr(residual), _ptr(cu_dev), nseq, _ptr(z), _ptr(y), _ptr(mean), _ptr(rstd),

@@ -71,33 +71,25 @@ int sp_region_time_next_call(void* start_event, void* stop_event) {
   return SPR_OK;
 }
 
-int sp_region_fwd(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p_drop,
-                  const void* gamma, const void* beta,
-                  int32_t norm, int32_t dtype, int32_t rank, uint64_t seed,
-                  const void* partials, int64_t slab_stride,
-                  const void* bias, const void* residual,
-                  const int32_t* cu_seqlens, int32_t nseq,
-                  void* z, void* y, float* mean, float* rstd,
-                  uint8_t* mask_out,
-                  void* stream) {
-  ClearLaunchEvents clear_hook;
-  int64_t T = 0;
-  int st = check_shape(b, s, h, t, norm, dtype, &T);
-  if (st != SPR_OK) return st;
-  if (!(eps > 0.0f) || !std::isfinite(eps)) return SPR_ERR_INVALID_ARG;
-  if (!(p_drop >= 0.0f && p_drop < 1.0f)) return SPR_ERR_INVALID_ARG;
-  if (rank < 0 || rank >= t) return SPR_ERR_INVALID_ARG;
-  if (cu_seqlens != nullptr && (nseq < 1 || b != 1)) return SPR_ERR_INVALID_ARG;
-  if (nseq < 0) return SPR_ERR_INVALID_ARG;
-  if (T == 0) return SPR_OK;
+}  // extern "C"
+
+namespace {
+
+// The forward's checks and parameters, shared by the strided and the
+// pointer-table entry points; slabs[k] is slab k's device pointer.
+int run_fwd(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p_drop, const void* gamma,
+            const void* beta, int32_t norm, int32_t dtype, int32_t rank, uint64_t seed, const void* const* slabs,
+            const void* bias, const void* residual, const int32_t* cu_seqlens, int32_t nseq, void* z, void* y,
+            float* mean, float* rstd, uint8_t* mask_out, void* stream) {
+  for (int32_t k = 0; k < t && k < SPR_MAX_T_SLABS; ++k) {
+    if (slabs[k] == nullptr) return SPR_ERR_INVALID_ARG;
+    if (!aligned16(slabs[k])) return SPR_ERR_ALIGNMENT;
+  }
   const bool ln = norm == SPR_LAYERNORM;
-  if (!partials || !gamma || !z || !y || !rstd) return SPR_ERR_INVALID_ARG;
+  if (!gamma || !z || !y || !rstd) return SPR_ERR_INVALID_ARG;
   if (ln != (mean != nullptr)) return SPR_ERR_INVALID_ARG;
   if (!ln && beta != nullptr) return SPR_ERR_INVALID_ARG;
-  if (slab_stride < T * h) return SPR_ERR_INVALID_ARG;
-  const int64_t eb = dtype == SPR_BF16 ? 2 : 4;
-  if ((slab_stride * eb) % 16 != 0) return SPR_ERR_ALIGNMENT;
-  for (const void* ptr : {partials, gamma, static_cast<const void*>(z), static_cast<const void*>(y),
+  for (const void* ptr : {gamma, static_cast<const void*>(z), static_cast<const void*>(y),
                           static_cast<const void*>(rstd)})
     if (!aligned16(ptr)) return SPR_ERR_ALIGNMENT;
   for (const void* ptr : {beta, bias, residual, static_cast<const void*>(mean), static_cast<const void*>(mask_out)})
@@ -105,8 +97,7 @@ int sp_region_fwd(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p
   if (cu_seqlens != nullptr && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return SPR_ERR_ALIGNMENT;
 
   spr::FwdParams p{};
-  p.partials = partials;
-  p.slab_stride = slab_stride;
+  for (int32_t k = 0; k < t; ++k) p.slab[k] = slabs[k];
   p.bias = bias;
   p.residual = residual;
   p.gamma = gamma;
@@ -118,7 +109,7 @@ int sp_region_fwd(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p
   p.mean = mean;
   p.rstd = rstd;
   p.mask = mask_out;
-  p.T = T;
+  p.T = b * (s / t);
   p.h = static_cast<int32_t>(h);
   p.t = t;
   p.rank = rank;
@@ -131,6 +122,66 @@ int sp_region_fwd(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p
   p.key0 = static_cast<uint32_t>(seed);
   p.key1 = static_cast<uint32_t>(seed >> 32);
   return hip_status(spr::launch_fwd(p, dtype, static_cast<hipStream_t>(stream)));
+}
+
+// Scalar checks common to both forward entry points; sets T.
+int check_fwd_scalars(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p_drop, int32_t norm,
+                      int32_t dtype, int32_t rank, const int32_t* cu_seqlens, int32_t nseq, int64_t* T) {
+  const int st = check_shape(b, s, h, t, norm, dtype, T);
+  if (st != SPR_OK) return st;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return SPR_ERR_INVALID_ARG;
+  if (!(p_drop >= 0.0f && p_drop < 1.0f)) return SPR_ERR_INVALID_ARG;
+  if (rank < 0 || rank >= t) return SPR_ERR_INVALID_ARG;
+  if (cu_seqlens != nullptr && (nseq < 1 || b != 1)) return SPR_ERR_INVALID_ARG;
+  if (nseq < 0) return SPR_ERR_INVALID_ARG;
+  return SPR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sp_region_fwd(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p_drop,
+                  const void* gamma, const void* beta,
+                  int32_t norm, int32_t dtype, int32_t rank, uint64_t seed,
+                  const void* partials, int64_t slab_stride,
+                  const void* bias, const void* residual,
+                  const int32_t* cu_seqlens, int32_t nseq,
+                  void* z, void* y, float* mean, float* rstd,
+                  uint8_t* mask_out,
+                  void* stream) {
+  ClearLaunchEvents clear_hook;
+  int64_t T = 0;
+  const int st = check_fwd_scalars(b, s, h, t, eps, p_drop, norm, dtype, rank, cu_seqlens, nseq, &T);
+  if (st != SPR_OK) return st;
+  if (T == 0) return SPR_OK;
+  if (!partials) return SPR_ERR_INVALID_ARG;
+  if (slab_stride < T * h) return SPR_ERR_INVALID_ARG;
+  const int64_t eb = dtype == SPR_BF16 ? 2 : 4;
+  if ((slab_stride * eb) % 16 != 0) return SPR_ERR_ALIGNMENT;
+  const void* slabs[SPR_MAX_T_SLABS];
+  for (int32_t k = 0; k < t; ++k) slabs[k] = static_cast<const char*>(partials) + k * slab_stride * eb;
+  return run_fwd(b, s, h, t, eps, p_drop, gamma, beta, norm, dtype, rank, seed, slabs, bias, residual, cu_seqlens,
+                 nseq, z, y, mean, rstd, mask_out, stream);
+}
+
+int sp_region_fwd_slabs(int64_t b, int64_t s, int64_t h, int32_t t, float eps, float p_drop,
+                        const void* gamma, const void* beta,
+                        int32_t norm, int32_t dtype, int32_t rank, uint64_t seed,
+                        const void* const* slabs,
+                        const void* bias, const void* residual,
+                        const int32_t* cu_seqlens, int32_t nseq,
+                        void* z, void* y, float* mean, float* rstd,
+                        uint8_t* mask_out,
+                        void* stream) {
+  ClearLaunchEvents clear_hook;
+  int64_t T = 0;
+  const int st = check_fwd_scalars(b, s, h, t, eps, p_drop, norm, dtype, rank, cu_seqlens, nseq, &T);
+  if (st != SPR_OK) return st;
+  if (T == 0) return SPR_OK;
+  if (slabs == nullptr) return SPR_ERR_INVALID_ARG;
+  return run_fwd(b, s, h, t, eps, p_drop, gamma, beta, norm, dtype, rank, seed, slabs, bias, residual, cu_seqlens,
+                 nseq, z, y, mean, rstd, mask_out, stream);
 }
 
 int64_t sp_region_partials_stride(int64_t n_local_tokens, int64_t h, int32_t dtype) {

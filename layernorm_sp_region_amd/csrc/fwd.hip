@@ -91,8 +91,11 @@ __global__ __launch_bounds__(WPR == 1 ? 64 * kRowsPerBlockW1 : 64 * WPR, 2) void
   const int h = p.h;
   const int nvec = h / V;
   const int64_t row_off = row * static_cast<int64_t>(h) * EB;   // bytes
-  const int64_t slab_bytes = p.slab_stride * EB;
-  const char* prow = static_cast<const char*>(p.partials) + row_off;
+  // Each slab through its own base pointer (wave-uniform), so slabs may sit
+  // in separate buffers -- or, peer-mapped, in other GPUs' memory.
+  const char* srow[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) srow[s] = static_cast<const char*>(p.slab[s]) + row_off;
 
   // Every memory instruction below is unconditional.  The waitcnt pass
   // cannot count loads or stores issued under a branch, and would then wait
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(WPR == 1 ? 64 * kRowsPerBlockW1 : 64 * WPR, 2) void
   auto issue = [&](Slot<NS>& sl, int k) {
     const uint32_t o = lane_off(k);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) sl.s[s] = ld16_stream(prow + s * slab_bytes + o);
+    for (int s = 0; s < NS; ++s) sl.s[s] = ld16_stream(srow[s] + o);
     sl.r = ld16_stream(rrow + o);
     sl.b = ld16(biasp + o);
   };

@@ -29,8 +29,7 @@ inline void launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t stream, K
 
 // Parameters of one forward launch (validated by the ABI layer).
 struct FwdParams {
-  const void* partials;   // t slabs of [T][h]
-  int64_t slab_stride;    // elements between slabs
+  const void* slab[8];    // slab k: [T][h] of TP rank k's partial (k < t), anywhere in device memory
   const void* bias;       // [h] or null
   const void* residual;   // [T][h] or null
   const void* gamma;      // [h]

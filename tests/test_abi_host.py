@@ -132,6 +132,34 @@ def test_fwd_rejects(lib, over, status):
     assert call_fwd(lib, fwd_args(**over)) == status
 
 
+def call_fwd_slabs(lib, a, slabs):
+    table = None if slabs is None else (ctypes.c_void_p * len(slabs))(*slabs)
+    return lib.sp_region_fwd_slabs(a["b"], a["s"], a["h"], a["t"], a["eps"], a["p"], a["gamma"], a["beta"],
+                                   a["norm"], a["dtype"], a["rank"], a["seed"], table, a["bias"], a["residual"],
+                                   a["cu"], a["nseq"], a["z"], a["y"], a["mean"], a["rstd"], a["mask"], a["stream"])
+
+
+# The strided form's argument checks, except those about the stride itself,
+# apply unchanged to the pointer-table form.
+SLAB_TABLE_CASES = [c for c in FWD_CASES if not ({"partials", "slab_stride"} & set(c[0]))]
+
+
+@pytest.mark.parametrize("over,status", SLAB_TABLE_CASES, ids=[str(c[0]) for c in SLAB_TABLE_CASES])
+def test_fwd_slabs_rejects(lib, over, status):
+    a = fwd_args(**over)
+    table = [P + 4096 * k for k in range(max(1, min(a["t"], 8)))]   # t entries (t > 8 is rejected first)
+    assert call_fwd_slabs(lib, a, table) == status
+
+
+def test_fwd_slabs_table_checks(lib):
+    four = [P, P + 4096, P + 8192, P + 65536]
+    assert call_fwd_slabs(lib, fwd_args(), None) == INVALID
+    assert call_fwd_slabs(lib, fwd_args(), [P, None, P, P]) == INVALID
+    assert call_fwd_slabs(lib, fwd_args(), [P, P + 8, P, P]) == ALIGN
+    assert call_fwd_slabs(lib, fwd_args(s=0), None) == spr.SPR_OK          # T = 0: nothing to read
+    assert call_fwd_slabs(lib, fwd_args(p=2.0), four) == INVALID
+
+
 def test_fwd_empty_shard_is_noop(lib):
     # T == 0: OK without touching any pointer (all NULL).
     a = fwd_args(s=0, partials=None, gamma=None, beta=None, residual=None, z=None, y=None, mean=None, rstd=None)

@@ -314,3 +314,35 @@ def test_every_slot_count(cuda_device, shape):
     inp = W.make_inputs(w)
     gpu = run_gpu(inp, w, rank, cuda_device, recommended_stride=True)
     compare(w, inp, gpu, rank)
+
+
+@pytest.mark.parametrize("name", ["page_demo", "shard70b", "odd_t3_h520"])
+def test_slab_pointer_table_matches_strided(cuda_device, name):
+    """sp_region_fwd_slabs with the t slabs in t separate allocations (made in
+    reverse order, so no stride relates them) gives the strided form's bits:
+    z, y, mean, rstd and the mask."""
+    import torch
+    if name == "odd_t3_h520":
+        w = W.custom("odd_t3_h520", h=520, t=3, s=3 * 37, b=2, p_drop=0.25)
+        inp = W.make_inputs(w)
+    else:
+        w = W.BY_NAME[name]
+        inp = inputs_for(w)
+    log(f"[slab-table] {name}")
+    t = lambda a: W.as_torch(a, cuda_device)
+    P = t(inp["partials"])
+    separate = [None] * w.t
+    for k in reversed(range(w.t)):
+        separate[k] = torch.empty_like(P[k]).copy_(P[k])
+    kw = dict(bias=t(inp["bias"]), residual=t(inp["residual"]), b=inp["b"], s=inp["s"], t=w.t, rank=w.t - 1,
+              eps=w.eps, p_drop=w.p_drop, seed=inp["seed"], norm=w.norm, cu_seqlens=inp["cu_seqlens"],
+              return_mask=True)
+    a = spr.fwd(P, t(inp["gamma"]), t(inp["beta"]), **kw)
+    b = spr.fwd(separate, t(inp["gamma"]), t(inp["beta"]), **kw)
+    torch.cuda.synchronize()
+    for k in ("z", "y", "mean", "rstd", "mask"):
+        x, y_ = getattr(a, k), getattr(b, k)
+        if x is None:
+            assert y_ is None
+            continue
+        assert torch.equal(x.view(torch.uint8), y_.view(torch.uint8)), k
