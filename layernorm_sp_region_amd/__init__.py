@@ -436,3 +436,57 @@ def shard_layout(lengths, t: int):
                                                T.ctypes.data)
     _check("sp_region_shard_layout", st)
     return padded[:a.size].tolist(), cu.tolist(), int(T[0])
+
+
+# ---------------------------------------------------------------------------
+# torch.autograd wiring (argument marshalling around fwd / bwd_dropout).
+# ---------------------------------------------------------------------------
+def _autograd_function():
+    import torch
+
+    class SPRegion(torch.autograd.Function):
+        """(partials [t][T][h], gamma, beta, bias, residual) -> (y, z).
+
+        Backward: y's gradient is dy, z's gradient (z is also the next
+        residual stream) is dres_in; returns the gradients of the slabs (the
+        same dpartial for every slab), gamma, beta, bias and residual."""
+
+        @staticmethod
+        def forward(ctx, partials, gamma, beta, bias, residual, cfg):
+            o = fwd(partials, gamma, beta, bias=bias, residual=residual, **cfg)
+            ctx.save_for_backward(o.z, o.mean, o.rstd, gamma)
+            ctx.cfg = cfg
+            ctx.shape = tuple(partials.shape)
+            ctx.flags = (beta is not None, bias is not None, residual is not None)
+            return o.y, o.z
+
+        @staticmethod
+        def backward(ctx, dy, dz):
+            z, mean, rstd, gamma = ctx.saved_tensors
+            cfg = ctx.cfg
+            has_beta, has_bias, has_res = ctx.flags
+            dy = torch.zeros_like(z) if dy is None else dy.contiguous()
+            g = bwd_dropout(dy, z, mean, rstd, gamma, b=cfg["b"], s=cfg["s"], t=cfg["t"], rank=cfg["rank"],
+                            p_drop=cfg["p_drop"], seed=cfg["seed"], norm=cfg.get("norm", "layernorm"),
+                            cu_seqlens=cfg.get("cu_seqlens"), dres_in=None if dz is None else dz.contiguous(),
+                            want_dbeta=has_beta, want_dbias=has_bias)
+            dpart = g.dpartial.unsqueeze(0).expand(ctx.shape)
+            return (dpart, g.dgamma.to(gamma.dtype), None if g.dbeta is None else g.dbeta.to(gamma.dtype),
+                    None if g.dbias is None else g.dbias.to(gamma.dtype), g.dx if has_res else None, None)
+
+    return SPRegion
+
+
+_SPREGION = None
+
+
+def region(partials, gamma, beta=None, *, bias=None, residual=None, b: int, s: int, t: int, rank: int,
+           eps: float, p_drop: float, seed: int, norm: Union[str, int] = "layernorm", cu_seqlens=None):
+    """Autograd-aware region: returns (y, z); gradients flow to partials (every
+    slab receives dpartial), gamma, beta, bias and residual.  dgamma, dbeta
+    and dbias are computed in float32 and returned in the parameters' dtype."""
+    global _SPREGION
+    if _SPREGION is None:
+        _SPREGION = _autograd_function()
+    cfg = dict(b=b, s=s, t=t, rank=rank, eps=eps, p_drop=p_drop, seed=seed, norm=norm, cu_seqlens=cu_seqlens)
+    return _SPREGION.apply(partials, gamma, beta, bias, residual, cfg)

@@ -145,3 +145,49 @@ def test_planned_buckets_end_to_end(cuda_device):
         torch.cuda.synchronize()
         ran += 1
     assert ran >= 2
+
+
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+def test_autograd_region_matches_torch_autograd(cuda_device, norm):
+    """spr.region under torch.autograd: the gradients of slabs, gamma, beta,
+    bias and residual for loss = sum(y*gy) + sum(z*gz) against torch's own
+    autograd in float64 on the CPU through the same forward (the oracle's
+    keep mask, float32 scale)."""
+    import torch
+    import torch.nn.functional as F
+    T, h, t, p, eps, seed = 24, 256, 3, 0.3, 1e-5, 0x1234
+    rng = np.random.default_rng(21)
+    P = rng.standard_normal((t, T, h)).astype(np.float32)
+    res = rng.standard_normal((T, h)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(h)).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, h).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(h)).astype(np.float32) if norm == "layernorm" else None
+    gy = rng.standard_normal((T, h)).astype(np.float32)
+    gz = rng.standard_normal((T, h)).astype(np.float32)
+    keep = ref.region_forward(P, t=t, rank=1, dtype="f32", norm=norm, eps=eps, p_drop=p, seed=seed, gamma=gamma,
+                              beta=beta, bias=bias, residual=res)["keep"]
+    scale = float(ref.dropout_scale(p))
+
+    c = lambda a: None if a is None else torch.from_numpy(a).double().requires_grad_(True)
+    Pc, gc, bc, biasc, rc = c(P), c(gamma), c(beta), c(bias), c(res)
+    acc = Pc.sum(0) + biasc
+    z = rc + torch.where(torch.from_numpy(keep), acc * scale, torch.zeros_like(acc))
+    if norm == "layernorm":
+        y = F.layer_norm(z, (h,), gc, bc, eps)
+    else:
+        y = z * torch.rsqrt((z * z).mean(-1, keepdim=True) + eps) * gc
+    (y * torch.from_numpy(gy).double()).sum().add((z * torch.from_numpy(gz).double()).sum()).backward()
+
+    g = lambda a: None if a is None else torch.from_numpy(a).to(cuda_device).requires_grad_(True)
+    Pg, gg, bg, biasg, rg = g(P), g(gamma), g(beta), g(bias), g(res)
+    yg, zg = spr.region(Pg, gg, bg, bias=biasg, residual=rg, b=1, s=t * T, t=t, rank=1, eps=eps, p_drop=p,
+                        seed=seed, norm=norm)
+    (yg * torch.from_numpy(gy).to(cuda_device)).sum().add((zg * torch.from_numpy(gz).to(cuda_device)).sum()).backward()
+    torch.cuda.synchronize()
+    for name, a, b in [("slabs", Pg, Pc), ("gamma", gg, gc), ("beta", bg, bc), ("bias", biasg, biasc),
+                       ("residual", rg, rc)]:
+        if a is None:
+            continue
+        got, want = a.grad.double().cpu(), b.grad
+        tol = 1e-4 * max(1.0, float(want.abs().max()))
+        assert float((got - want).abs().max()) <= tol, f"{name}: {float((got - want).abs().max()):.3e} > {tol:.3e}"
