@@ -278,3 +278,31 @@ def region_backward(dy, z, gamma, *, dtype, norm, eps, dres_in=None, rows=None, 
     if with_param_grads:
         out.update(dgamma=dgamma, dbeta=dbeta if norm == LAYERNORM else None, A=A, B=B)
     return out
+
+
+def accumulate_param_grads(main, step):
+    """Parameter gradients added into main-grad buffers (float64, unrounded).
+
+    Gradient accumulation over micro-batches: the parameter gradient of a
+    step is the sum over every token of every micro-batch, so each
+    micro-batch's backward adds its own column sums (dgamma, dbeta, dbias of
+    region_backward / dropout_backward) into buffers that persist across the
+    micro-batches instead of replacing them.  The pages do not describe this
+    step; it is the usual convention of mixed-precision training, where those
+    buffers are float32.
+
+    main: dict name -> [h] array (the buffers before the call) or None.
+    step: dict name -> float64 [h] array (this micro-batch's sums) or None.
+    Returns dict name -> float64 [h]: main + step for every name whose main
+    buffer is given (a name without a buffer is not accumulated).
+    """
+    out = {}
+    for name, buf in main.items():
+        if buf is None:
+            out[name] = None
+            continue
+        add = step.get(name)
+        if add is None:
+            raise ValueError(f"no gradient {name!r} to accumulate")
+        out[name] = np.asarray(buf, dtype=np.float64) + np.asarray(add, dtype=np.float64)
+    return out

@@ -383,3 +383,42 @@ def check_dropout_backward_special_cases(seed=13, T=20, h=24, t=4, rank=2, R=R):
     for j in range(h):
         assert out["dbias"][j] == math.fsum(out["dpartial"][:, j]) or \
             abs(out["dbias"][j] - math.fsum(out["dpartial"][:, j])) <= 1e-12 * out["C"][j]
+
+
+def check_accumulate_split_batches(seed=14, T=23, h=40, t=2, rank=1, cuts=(0, 7, 8, 23), R=R):
+    """Gradient accumulation: a batch's rows taken as micro-batches of
+    unequal sizes (one of a single row), each micro-batch's parameter
+    gradients added in turn into random float32 main buffers, equals those
+    buffers plus the gradients of the whole batch in one backward -- the
+    parameter gradient is a plain sum over tokens, so splitting the tokens
+    splits the sum."""
+    rng = _rng(seed)
+    z = rng.standard_normal((T, h)).astype(np.float32)
+    dy = rng.standard_normal((T, h)).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, h).astype(np.float32)
+    main0 = {k: rng.standard_normal(h).astype(np.float32) for k in ("dgamma", "dbeta", "dbias")}
+
+    def grads(rows):
+        b = R.region_backward(dy, z, gamma, dtype="f32", norm="layernorm", eps=1e-5, rows=rows)
+        d = R.dropout_backward(b["dx"], t=t, rank=rank, p_drop=0.3, seed=9, T=T, rows=rows)
+        return dict(dgamma=b["dgamma"], dbeta=b["dbeta"], dbias=d["dbias"]), b["A"] + b["B"] + d["C"]
+
+    acc = dict(main0)
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        acc = R.accumulate_param_grads(acc, grads(np.arange(a, b))[0])
+    full, scale = grads(np.arange(T))
+    for k in main0:
+        ref = main0[k].astype(np.float64) + full[k]
+        assert np.max(np.abs(acc[k] - ref) / (scale + np.abs(main0[k]))) < 1e-12, k
+
+
+def check_accumulate_identities(seed=15, h=24, R=R):
+    """Zero buffers take the step's gradients exactly, a zero step leaves the
+    buffers exactly, and a name without a buffer stays absent."""
+    rng = _rng(seed)
+    step = dict(dgamma=rng.standard_normal(h), dbeta=rng.standard_normal(h))
+    main = dict(dgamma=rng.standard_normal(h).astype(np.float32), dbeta=None)
+    out = R.accumulate_param_grads(dict(dgamma=np.zeros(h, np.float32), dbeta=np.zeros(h, np.float32)), step)
+    assert np.array_equal(out["dgamma"], step["dgamma"]) and np.array_equal(out["dbeta"], step["dbeta"])
+    out = R.accumulate_param_grads(main, dict(dgamma=np.zeros(h), dbeta=np.zeros(h)))
+    assert np.array_equal(out["dgamma"], main["dgamma"].astype(np.float64)) and out["dbeta"] is None

@@ -83,6 +83,16 @@ REGION_MUTATIONS = [
     ("dropout_bwd_dbias_from_dx", "return dict(dpartial=dpartial, dbias=dpartial.sum(axis=0),",
      "return dict(dpartial=dpartial, dbias=dx.sum(axis=0),",
      lambda R: pins.check_dropout_backward_finite_differences(R=R)),
+    ("accumulate_overwrites", "np.asarray(buf, dtype=np.float64) + np.asarray(add, dtype=np.float64)",
+     "0.0 * np.asarray(buf, dtype=np.float64) + np.asarray(add, dtype=np.float64)",
+     lambda R: pins.check_accumulate_split_batches(R=R)),
+    ("accumulate_subtracts", "np.asarray(buf, dtype=np.float64) + np.asarray(add, dtype=np.float64)",
+     "np.asarray(buf, dtype=np.float64) - np.asarray(add, dtype=np.float64)",
+     lambda R: pins.check_accumulate_split_batches(R=R)),
+    ("accumulate_rounds_to_bf16", "np.asarray(buf, dtype=np.float64) + np.asarray(add, dtype=np.float64)",
+     "decode(encode((np.asarray(buf, dtype=np.float64) + np.asarray(add, dtype=np.float64)).astype(np.float32), "
+     "'bf16'), 'bf16').astype(np.float64)",
+     lambda R: pins.check_accumulate_split_batches(R=R)),
 ]
 
 

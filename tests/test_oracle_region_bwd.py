@@ -30,3 +30,11 @@ def test_dropout_backward_finite_differences(norm, ragged):
 
 def test_dropout_backward_special_cases():
     pins.check_dropout_backward_special_cases()
+
+
+def test_accumulate_split_batches():
+    pins.check_accumulate_split_batches()
+
+
+def test_accumulate_identities():
+    pins.check_accumulate_identities()
