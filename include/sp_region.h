@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SP_REGION_ABI_VERSION 1
+#define SP_REGION_ABI_VERSION 2   /* 2 added sp_region_bwd_accumulate */
 
 enum sp_region_status {
   SPR_OK = 0,
@@ -252,6 +252,42 @@ int sp_region_bwd_dropout(int64_t b, int64_t s, int64_t h, int32_t t,
                           void* dx, void* dpartial, float* dgamma, float* dbeta, float* dbias,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * Backward with the parameter gradients accumulated into float32 main-grad
+ * buffers, for gradient accumulation over micro-batches: the step's gradient
+ * of gamma, beta and the bias sums over the tokens of every micro-batch, so
+ * each micro-batch's backward adds its own sums into buffers that persist
+ * across them.  The pages do not describe this step; float32 main-grad
+ * buffers are the usual convention of mixed-precision training.
+ *
+ *   All arguments as in sp_region_bwd_dropout, except:
+ *   dpartial     out [T][h] or NULL.  NULL: no gradient through the dropout
+ *                and the slab sum (dbias must then be NULL too when T > 0);
+ *                the dropout arguments are still checked but otherwise
+ *                unused, and the call is sp_region_bwd with accumulation.
+ *   dgamma, dbeta, dbias
+ *                in/out float32 [h] (dbeta and dbias may be NULL): element j
+ *                becomes float32(old_j + sum_j), where sum_j is, bit for bit,
+ *                what sp_region_bwd_dropout (dpartial given) or sp_region_bwd
+ *                (dpartial NULL) writes for the same inputs.
+ *   workspace    >= sp_region_bwd_dropout_workspace_bytes(T, h) bytes when
+ *                dpartial is given, else >= sp_region_bwd_workspace_bytes(T, h).
+ *
+ * dx and dpartial are overwritten, as in the other calls.  T == 0 launches
+ * nothing and leaves every buffer as it was.  The buffers are read and
+ * written by the call's last kernel, so calls that accumulate into the same
+ * buffers must be ordered (one stream, or events between streams).
+ */
+int sp_region_bwd_accumulate(int64_t b, int64_t s, int64_t h, int32_t t,
+                             const void* gamma, int32_t norm, int32_t dtype,
+                             const void* dy, const void* z, const float* mean, const float* rstd,
+                             const void* dres_in,
+                             float p_drop, int32_t rank, uint64_t seed,
+                             const int32_t* cu_seqlens, int32_t nseq,
+                             void* dx, void* dpartial, float* dgamma, float* dbeta, float* dbias,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* ------------------------------------------------------------------------
  * Host-side batch planning (no device work; pointers are HOST pointers).

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libsp_region.so")
 SPR_OK, SPR_ERR_INVALID_ARG, SPR_ERR_UNSUPPORTED, SPR_ERR_ALIGNMENT, SPR_ERR_HIP = range(5)
 SPR_F32, SPR_BF16 = 0, 1
 SPR_LAYERNORM, SPR_RMSNORM = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 # Every symbol include/sp_region.h declares, with its ctypes signature.
 _VP, _I64, _I32, _U64, _F32, _SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64,
@@ -47,6 +47,9 @@ SIGNATURES = {
     "sp_region_bwd_dropout": (ctypes.c_int, [_I64, _I64, _I64, _I32, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
                                              _F32, _I32, _U64, _VP, _I32,
                                              _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "sp_region_bwd_accumulate": (ctypes.c_int, [_I64, _I64, _I64, _I32, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
+                                                _F32, _I32, _U64, _VP, _I32,
+                                                _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "sp_region_hbm_copy": (ctypes.c_int, [_VP, _VP, _SZ, _VP]),
     "sp_region_cv_within": (ctypes.c_int, [_VP, _I32, _I32, _VP]),
     "sp_region_bucket_by_tokens": (ctypes.c_int, [_VP, _I32, _I32, _I64, _VP, _VP, _VP]),
@@ -264,9 +267,12 @@ def _cu_on_device(cu_seqlens, T, dev):
 
 
 def bwd(dy, z, mean, rstd, gamma, *, b: int, s: int, t: int, norm: Union[str, int] = "layernorm",
-        dres_in=None, want_dbeta: bool = True, workspace=None, out: Optional[BwdOut] = None) -> BwdOut:
+        dres_in=None, want_dbeta: bool = True, workspace=None, out: Optional[BwdOut] = None,
+        accumulate: bool = False) -> BwdOut:
     """Backward of the region's normalisation.  Returns BwdOut(dx, dgamma, dbeta)
-    (dbeta None for RMSNorm or when want_dbeta is False)."""
+    (dbeta None for RMSNorm or when want_dbeta is False).  accumulate=True
+    adds the parameter gradients into out's float32 dgamma/dbeta (main-grad
+    buffers, sp_region_bwd_accumulate) instead of overwriting them."""
     import torch
     lib = load_library()
     nc = _norm_code(norm)
@@ -290,6 +296,8 @@ def bwd(dy, z, mean, rstd, gamma, *, b: int, s: int, t: int, norm: Union[str, in
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
     _require(workspace, "workspace", dev, torch.uint8)
     if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs out= holding the main-grad buffers")
         dx = torch.empty((T, h), dtype=dt, device=dev)
         dgamma = torch.empty((h,), dtype=torch.float32, device=dev)
         dbeta = torch.empty((h,), dtype=torch.float32, device=dev) if (ln and want_dbeta) else None
@@ -299,10 +307,17 @@ def bwd(dy, z, mean, rstd, gamma, *, b: int, s: int, t: int, norm: Union[str, in
         _require(dgamma, "dgamma", dev, torch.float32, (h,))
         _require(dbeta, "dbeta", dev, torch.float32, (h,))
     stream = torch.cuda.current_stream(dev).cuda_stream
-    st = lib.sp_region_bwd(b, s, h, t, _ptr(gamma), nc, dcode, _ptr(dy), _ptr(z), _ptr(mean if ln else None),
-                           _ptr(rstd), _ptr(dres_in), _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(workspace),
-                           workspace.numel(), stream)
-    _check("sp_region_bwd", st)
+    if accumulate:
+        st = lib.sp_region_bwd_accumulate(b, s, h, t, _ptr(gamma), nc, dcode, _ptr(dy), _ptr(z),
+                                          _ptr(mean if ln else None), _ptr(rstd), _ptr(dres_in), 0.0, 0, 0, None, 0,
+                                          _ptr(dx), None, _ptr(dgamma), _ptr(dbeta), None, _ptr(workspace),
+                                          workspace.numel(), stream)
+        _check("sp_region_bwd_accumulate", st)
+    else:
+        st = lib.sp_region_bwd(b, s, h, t, _ptr(gamma), nc, dcode, _ptr(dy), _ptr(z), _ptr(mean if ln else None),
+                               _ptr(rstd), _ptr(dres_in), _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(workspace),
+                               workspace.numel(), stream)
+        _check("sp_region_bwd", st)
     return BwdOut(dx, dgamma, dbeta)
 
 
@@ -315,10 +330,12 @@ BwdDropoutOut = namedtuple("BwdDropoutOut", "dx dpartial dgamma dbeta dbias")
 
 def bwd_dropout(dy, z, mean, rstd, gamma, *, b: int, s: int, t: int, rank: int, p_drop: float, seed: int,
                 norm: Union[str, int] = "layernorm", cu_seqlens=None, dres_in=None, want_dbeta: bool = True,
-                want_dbias: bool = True, workspace=None, out: Optional["BwdDropoutOut"] = None) -> "BwdDropoutOut":
+                want_dbias: bool = True, workspace=None, out: Optional["BwdDropoutOut"] = None,
+                accumulate: bool = False) -> "BwdDropoutOut":
     """Backward of the region through the dropout and the slab sum: BwdOut's
     dx, dgamma, dbeta plus dpartial (the gradient of every slab) and dbias.
-    p_drop, rank, seed and cu_seqlens are the forward's."""
+    p_drop, rank, seed and cu_seqlens are the forward's.  accumulate=True
+    adds dgamma/dbeta/dbias into out's float32 buffers (main gradients)."""
     import torch
     lib = load_library()
     nc = _norm_code(norm)
@@ -343,6 +360,8 @@ def bwd_dropout(dy, z, mean, rstd, gamma, *, b: int, s: int, t: int, rank: int, 
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
     _require(workspace, "workspace", dev, torch.uint8)
     if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs out= holding the main-grad buffers")
         dx = torch.empty((T, h), dtype=dt, device=dev)
         dpartial = torch.empty((T, h), dtype=dt, device=dev)
         dgamma = torch.empty((h,), dtype=torch.float32, device=dev)
@@ -356,11 +375,12 @@ def bwd_dropout(dy, z, mean, rstd, gamma, *, b: int, s: int, t: int, rank: int, 
         _require(dbeta, "dbeta", dev, torch.float32, (h,))
         _require(dbias, "dbias", dev, torch.float32, (h,))
     stream = torch.cuda.current_stream(dev).cuda_stream
-    st = lib.sp_region_bwd_dropout(b, s, h, t, _ptr(gamma), nc, dcode, _ptr(dy), _ptr(z),
-                                   _ptr(mean if ln else None), _ptr(rstd), _ptr(dres_in), float(p_drop), rank,
-                                   int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(cu_dev), nseq, _ptr(dx), _ptr(dpartial),
-                                   _ptr(dgamma), _ptr(dbeta), _ptr(dbias), _ptr(workspace), workspace.numel(), stream)
-    _check("sp_region_bwd_dropout", st)
+    fn = "sp_region_bwd_accumulate" if accumulate else "sp_region_bwd_dropout"
+    st = getattr(lib, fn)(b, s, h, t, _ptr(gamma), nc, dcode, _ptr(dy), _ptr(z),
+                          _ptr(mean if ln else None), _ptr(rstd), _ptr(dres_in), float(p_drop), rank,
+                          int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(cu_dev), nseq, _ptr(dx), _ptr(dpartial),
+                          _ptr(dgamma), _ptr(dbeta), _ptr(dbias), _ptr(workspace), workspace.numel(), stream)
+    _check(fn, st)
     return BwdDropoutOut(dx, dpartial, dgamma, dbeta, dbias)
 
 

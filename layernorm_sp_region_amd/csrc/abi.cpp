@@ -249,6 +249,35 @@ int prepare_bwd(int64_t b, int64_t s, int64_t h, int32_t t, const void* gamma, i
   return SPR_OK;
 }
 
+// The forward's dropout arguments as the backward takes them (same checks).
+int check_dropout_args(int64_t b, int32_t t, float p_drop, int32_t rank, const int32_t* cu_seqlens, int32_t nseq) {
+  if (!(p_drop >= 0.0f && p_drop < 1.0f)) return SPR_ERR_INVALID_ARG;
+  if (rank < 0 || rank >= t) return SPR_ERR_INVALID_ARG;
+  if (cu_seqlens != nullptr && (nseq < 1 || b != 1)) return SPR_ERR_INVALID_ARG;
+  if (nseq < 0) return SPR_ERR_INVALID_ARG;
+  if (cu_seqlens != nullptr && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return SPR_ERR_ALIGNMENT;
+  return SPR_OK;
+}
+
+// Gradient through the dropout and the slab sum: dpartial (rows kernel) and
+// the dbias partials, with the mask parameters the forward used.
+void set_dropout(spr::BwdParams* p, int32_t t, float p_drop, int32_t rank, uint64_t seed,
+                 const int32_t* cu_seqlens, int32_t nseq, void* dpartial, float* dbias) {
+  if (p->T > 0) p->dpartial = dpartial;
+  p->dbias = dbias;
+  if (dbias) p->slot_dbias = p->nparts++;
+  p->cu = cu_seqlens;
+  p->nseq = nseq;
+  p->t = t;
+  p->rank = rank;
+  const double pd = static_cast<double>(p_drop);
+  p->drop = p_drop > 0.0f ? 1 : 0;
+  p->scale = static_cast<float>(1.0 / (1.0 - pd));
+  p->thr = static_cast<uint32_t>(std::floor(pd * 4294967296.0));
+  p->key0 = static_cast<uint32_t>(seed);
+  p->key1 = static_cast<uint32_t>(seed >> 32);
+}
+
 }  // namespace
 
 extern "C" {
@@ -279,29 +308,38 @@ int sp_region_bwd_dropout(int64_t b, int64_t s, int64_t h, int32_t t,
                           void* stream) {
   ClearLaunchEvents clear_hook;
   spr::BwdParams p;
-  const int st = prepare_bwd(b, s, h, t, gamma, norm, dtype, dy, z, mean, rstd, dres_in, dx, dgamma, dbeta,
-                             workspace, workspace_bytes, true, &p);
+  int st = prepare_bwd(b, s, h, t, gamma, norm, dtype, dy, z, mean, rstd, dres_in, dx, dgamma, dbeta,
+                       workspace, workspace_bytes, true, &p);
   if (st != SPR_OK) return st;
-  if (!(p_drop >= 0.0f && p_drop < 1.0f)) return SPR_ERR_INVALID_ARG;
-  if (rank < 0 || rank >= t) return SPR_ERR_INVALID_ARG;
-  if (cu_seqlens != nullptr && (nseq < 1 || b != 1)) return SPR_ERR_INVALID_ARG;
-  if (nseq < 0) return SPR_ERR_INVALID_ARG;
+  st = check_dropout_args(b, t, p_drop, rank, cu_seqlens, nseq);
+  if (st != SPR_OK) return st;
   if (p.T > 0 && dpartial == nullptr) return SPR_ERR_INVALID_ARG;
   if (!aligned16_or_null(dpartial) || !aligned16_or_null(dbias)) return SPR_ERR_ALIGNMENT;
-  if (cu_seqlens != nullptr && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return SPR_ERR_ALIGNMENT;
-  if (p.T > 0) p.dpartial = dpartial;
-  p.dbias = dbias;
-  if (dbias) p.slot_dbias = p.nparts++;
-  p.cu = cu_seqlens;
-  p.nseq = nseq;
-  p.t = t;
-  p.rank = rank;
-  const double pd = static_cast<double>(p_drop);
-  p.drop = p_drop > 0.0f ? 1 : 0;
-  p.scale = static_cast<float>(1.0 / (1.0 - pd));
-  p.thr = static_cast<uint32_t>(std::floor(pd * 4294967296.0));
-  p.key0 = static_cast<uint32_t>(seed);
-  p.key1 = static_cast<uint32_t>(seed >> 32);
+  set_dropout(&p, t, p_drop, rank, seed, cu_seqlens, nseq, dpartial, dbias);
+  return hip_status(spr::launch_bwd(p, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int sp_region_bwd_accumulate(int64_t b, int64_t s, int64_t h, int32_t t,
+                             const void* gamma, int32_t norm, int32_t dtype,
+                             const void* dy, const void* z, const float* mean, const float* rstd,
+                             const void* dres_in,
+                             float p_drop, int32_t rank, uint64_t seed,
+                             const int32_t* cu_seqlens, int32_t nseq,
+                             void* dx, void* dpartial, float* dgamma, float* dbeta, float* dbias,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  ClearLaunchEvents clear_hook;
+  const bool with_dropout = dpartial != nullptr;
+  spr::BwdParams p;
+  int st = prepare_bwd(b, s, h, t, gamma, norm, dtype, dy, z, mean, rstd, dres_in, dx, dgamma, dbeta,
+                       workspace, workspace_bytes, with_dropout, &p);
+  if (st != SPR_OK) return st;
+  st = check_dropout_args(b, t, p_drop, rank, cu_seqlens, nseq);
+  if (st != SPR_OK) return st;
+  if (p.T > 0 && !with_dropout && dbias != nullptr) return SPR_ERR_INVALID_ARG;   // dbias needs dpartial
+  if (!aligned16_or_null(dpartial) || !aligned16_or_null(dbias)) return SPR_ERR_ALIGNMENT;
+  if (with_dropout) set_dropout(&p, t, p_drop, rank, seed, cu_seqlens, nseq, dpartial, dbias);
+  p.accumulate = 1;
   return hip_status(spr::launch_bwd(p, dtype, static_cast<hipStream_t>(stream)));
 }
 

@@ -252,7 +252,7 @@ static_assert(kBwdMaxBlocks % kGroups == 0, "groups must split the partials even
 // threadIdx.x % cw).  Every thread of the block calls this (it has barriers).
 template <int CQMAX, int NP>
 __device__ __forceinline__ void reduce_cols(const float* __restrict__ ws, int G, int64_t bstride, int64_t sstride,
-                                            int q0, int q1,
+                                            int q0, int q1, bool accumulate,
                                             float* const (&out)[NP]) {
   __shared__ float4 part[NP][kGroups][CQMAX];
   const int cw = static_cast<int>(blockDim.x) / kGroups;
@@ -303,6 +303,10 @@ __device__ __forceinline__ void reduce_cols(const float* __restrict__ ws, int G,
           const float4 x = part[j][i][cq];
           tot.x += x.x; tot.y += x.y; tot.z += x.z; tot.w += x.w;
         }
+        if (accumulate) {   // main gradient: old + this call's sum, one rounding
+          const float4 m = reinterpret_cast<const float4*>(out[j])[c4];
+          tot.x = m.x + tot.x; tot.y = m.y + tot.y; tot.z = m.z + tot.z; tot.w = m.w + tot.w;
+        }
         reinterpret_cast<float4*>(out[j])[c4] = tot;
       }
     }
@@ -318,6 +322,7 @@ constexpr int kColQuads = SPR_COLS_QPB;
 // Outputs of stage 2, slot order (dgamma, then dbeta / dbias where requested).
 struct ColOut {
   float* p[3];
+  int32_t accumulate;   // nonzero: out = old + sum
 };
 
 template <int NP>
@@ -329,7 +334,8 @@ __global__ __launch_bounds__(kColQuads * kGroups) void sp_region_bwd_cols_kernel
   float* out[NP];
 #pragma unroll
   for (int j = 0; j < NP; ++j) out[j] = o.p[j];
-  reduce_cols<kColQuads, NP>(ws, G, bstride, sstride, q0, q0 + kColQuads < nq ? q0 + kColQuads : nq, out);
+  reduce_cols<kColQuads, NP>(ws, G, bstride, sstride, q0, q0 + kColQuads < nq ? q0 + kColQuads : nq,
+                             o.accumulate != 0, out);
 }
 
 #ifndef SPR_BWD_MAX_THREADS
@@ -347,7 +353,7 @@ constexpr int ring_for() {
 }
 
 hipError_t launch_cols(const BwdParams& p, hipStream_t stream) {
-  ColOut o{{p.dgamma, nullptr, nullptr}};
+  ColOut o{{p.dgamma, nullptr, nullptr}, p.accumulate};
   int np = 1;
   if (p.slot_dbeta > 0) o.p[np++] = p.dbeta;
   if (p.slot_dbias > 0) o.p[np++] = p.dbias;
@@ -409,7 +415,9 @@ hipError_t launch_bwd(const BwdParams& params, int dtype, hipStream_t stream) {
     if (dtype == 1) return drop ? launch_rows<Bf16, true>(p, sh, stream) : launch_rows<Bf16, false>(p, sh, stream);
     return drop ? launch_rows<F32, true>(p, sh, stream) : launch_rows<F32, false>(p, sh, stream);
   }
-  // No rows: every output is 0 (every group of partials is empty).
+  // No rows: every output is 0 (every group of partials is empty); an
+  // accumulating call adds nothing and launches nothing.
+  if (p.accumulate) return hipSuccess;
   return launch_cols(p, stream);
 }
 

@@ -87,6 +87,9 @@ struct BwdParams {
   uint32_t thr;
   float scale;
   uint32_t key0, key1;
+  // Nonzero: dgamma / dbeta / dbias hold float32 main gradients and receive
+  // old + sum instead of sum.
+  int32_t accumulate;
 };
 
 // Number of row blocks of the backward's first stage (and of workspace

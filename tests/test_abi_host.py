@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.sp_region_abi_version() == spr.ABI_VERSION == 1
+    assert lib.sp_region_abi_version() == spr.ABI_VERSION == 2
     for st in range(5):
         assert lib.sp_region_strerror(st)
     assert lib.sp_region_strerror(99) == b"unknown status"
@@ -244,6 +244,40 @@ def test_bwd_dropout_empty_shard_needs_no_outputs(lib):
     # T = 0: nothing to launch beyond the zero-filled parameter gradients, which
     # need a device; without one only the argument checks can be exercised.
     assert call_bwd_dropout(lib, bwd_dropout_args(s=0, dpartial=None, ws=None, ws_bytes=0, p=2.0)) == INVALID
+
+
+def call_bwd_accumulate(lib, a):
+    return lib.sp_region_bwd_accumulate(a["b"], a["s"], a["h"], a["t"], a["gamma"], a["norm"], a["dtype"], a["dy"],
+                                        a["z"], a["mean"], a["rstd"], a["dres"], a["p"], a["rank"], a["seed"],
+                                        a["cu"], a["nseq"], a["dx"], a["dpartial"], a["dgamma"], a["dbeta"],
+                                        a["dbias"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+# With dpartial the accumulating call checks what sp_region_bwd_dropout checks;
+# without it, the two-slot workspace of sp_region_bwd suffices, dbias must be
+# NULL and the dropout arguments are still checked.
+BWD_ACCUMULATE_CASES = [c for c in BWD_DROPOUT_CASES if c[0] != dict(dpartial=None)] + [
+    (dict(dpartial=None), INVALID),                           # dbias without dpartial
+    (dict(dpartial=None, dbias=None, ws_bytes=WS2 - 1), INVALID),
+    (dict(dpartial=None, dbias=None, p=1.0), INVALID),
+    (dict(dpartial=None, dbias=None, rank=4), INVALID),
+    (dict(dpartial=None, dbias=None, dgamma=None), INVALID),
+    (dict(dpartial=None, dbias=None, dgamma=P + 4), ALIGN),
+]
+
+
+@pytest.mark.parametrize("over,status", BWD_ACCUMULATE_CASES, ids=[str(c[0]) for c in BWD_ACCUMULATE_CASES])
+def test_bwd_accumulate_rejects(lib, over, status):
+    assert call_bwd_accumulate(lib, bwd_dropout_args(**over)) == status
+
+
+def test_bwd_accumulate_empty_shard_launches_nothing(lib):
+    # T = 0 adds nothing to the main gradients: OK with no launch at all, so
+    # the (host) buffers here are never touched; the arguments are still checked.
+    a = bwd_dropout_args(s=0, dy=None, z=None, mean=None, rstd=None, dx=None, ws=None, ws_bytes=0)
+    assert call_bwd_accumulate(lib, dict(a, dpartial=None, dbias=None)) == spr.SPR_OK
+    assert call_bwd_accumulate(lib, a) == spr.SPR_OK
+    assert call_bwd_accumulate(lib, dict(a, p=2.0)) == INVALID
 
 
 def test_copy_rejects(lib):
