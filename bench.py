@@ -10,7 +10,7 @@ several input/output sets rotate so that consecutive steps do not hit the
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--sets R]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--sets R] [--no-extras]
   python bench.py --summarize-rocprof DIR   # rocprofv3 output -> text summary
   python bench.py --traffic FETCH_DIR WRITE_DIR   # --pmc runs -> HBM bytes per launch
 """
@@ -202,14 +202,14 @@ def run(args):
     ws = torch.empty(max(16, spr.workspace_bytes(T, h)), dtype=torch.uint8, device=dev)
     cu = torch.tensor(inp["cu_seqlens"], dtype=torch.int32, device=dev) if inp["cu_seqlens"] is not None else None
 
-    def step(i, ev=None):
+    def step(i, ev=None, p_drop=w.p_drop, rotate=True):
         # ev: four events; each region call stamps its first kernel's start and
         # last kernel's end into a pair of them from the dispatch packets.
-        s = sets[i % len(sets)]
+        s = sets[i % len(sets)] if rotate else sets[0]
         if ev is not None:
             spr.time_next_call(ev[0], ev[1])
         fo = spr.fwd(s["P"], gamma, beta, bias=bias, residual=s["res"], b=inp["b"], s=inp["s"], t=w.t, rank=0,
-                     eps=w.eps, p_drop=w.p_drop, seed=inp["seed"], norm=w.norm, cu_seqlens=cu, out=s["fo"])
+                     eps=w.eps, p_drop=p_drop, seed=inp["seed"], norm=w.norm, cu_seqlens=cu, out=s["fo"])
         if ev is not None:
             spr.time_next_call(ev[2], ev[3])
         spr.bwd(s["dy"], fo.z, fo.mean, fo.rstd, gamma, b=inp["b"], s=inp["s"], t=w.t, norm=w.norm,
@@ -251,41 +251,66 @@ def run(args):
     # events from its kernels' own dispatch packets (sp_region_time_next_call:
     # no marker packets, which cost the GPU ~3 us each, on the stream the
     # library launches on).  Each event is recorded once first so it exists.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for e in evs:
-        for x in e:
-            x.record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    elapsed_ev = time.perf_counter() - t1
+    def timestamped_steps(**kw):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for e in evs:
+            for x in e:
+                x.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, evs[i], **kw)
+        torch.cuda.synchronize()
+        elapsed_ev = time.perf_counter() - t1
+        fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+        bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+        return fwd_ms, bwd_ms, elapsed_ev
+
+    fwd_ms, bwd_ms, elapsed_ev = timestamped_steps()
+
+    def call_us(call, n):
+        """Durations (us) of n region calls, each stamping a pair of HIP events
+        from its own kernels' dispatch packets."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        for e in ev:
+            for x in e:
+                x.record()
+        for i in range(n):
+            spr.time_next_call(ev[i][0], ev[i][1])
+            call(i)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
 
     # The backward through the dropout and the slab sum (dpartial, dbias), on
-    # the same forward outputs: events around each of K launches.
+    # the same forward outputs.
     ws_d = torch.empty(max(16, spr.dropout_workspace_bytes(T, h)), dtype=torch.uint8, device=dev)
     douts = []
     for s in sets:
         bo = s["bo"]
         douts.append(spr.BwdDropoutOut(bo.dx, torch.empty_like(bo.dx), bo.dgamma, bo.dbeta,
                                        torch.empty(h, device=dev) if w.has_bias else None))
-    evd = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for e in evd:
-        for x in e:
-            x.record()
-    for i in range(args.steps):
+
+    def bwd_dropout_call(i):
         s, fo = sets[i % len(sets)], sets[i % len(sets)]["fo"]
-        spr.time_next_call(evd[i][0], evd[i][1])
         spr.bwd_dropout(s["dy"], fo.z, fo.mean, fo.rstd, gamma, b=inp["b"], s=inp["s"], t=w.t, rank=0,
                         p_drop=w.p_drop, seed=inp["seed"], norm=w.norm, cu_seqlens=cu, workspace=ws_d,
                         want_dbias=w.has_bias, out=douts[i % len(sets)])
-    torch.cuda.synchronize()
-    bwd_dropout_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evd]) * 1e3)
+
+    bwd_dropout_us = float(np.mean(call_us(bwd_dropout_call, args.steps)))
     del douts, ws_d
 
-    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    # The same steps with p = 0 (the forward's time prices the hash), and warm
+    # steps: one buffer set reused by every step, so whatever the Infinity
+    # Cache kept from the previous step is read from there.  Both run whole
+    # steps, since a forward's time depends on what the kernel before it left
+    # dirty in the caches.
+    extras = None
+    if not args.no_extras:
+        f0, b0, _ = timestamped_steps(p_drop=0.0)
+        fw, bw, _ = timestamped_steps(rotate=False)
+        extras = {"p0_step_us": {"fwd": float(f0.mean() * 1e3), "bwd": float(b0.mean() * 1e3)},
+                  "warm_one_set_step_us": {"fwd": float(fw.mean() * 1e3), "bwd": float(bw.mean() * 1e3)}}
+
     fb, bb = fwd_bytes(w, T), bwd_bytes(w, T)
     fwd_s = float(fwd_ms.mean()) * 1e-3
     achieved = fb / fwd_s / 1e9
@@ -318,6 +343,10 @@ def run(args):
         "step_us_timestamped_pass": elapsed_ev / args.steps * 1e6,
         "fwd_us": float(fwd_ms.mean() * 1e3),
         "bwd_us": float(bwd_ms.mean() * 1e3),
+        "fwd_us_p50_p95": [float(np.median(fwd_ms) * 1e3), float(np.percentile(fwd_ms, 95) * 1e3)],
+        "bwd_us_p50_p95": [float(np.median(bwd_ms) * 1e3), float(np.percentile(bwd_ms, 95) * 1e3)],
+        "extras": extras,
+        "workspace_bytes": {"bwd": spr.workspace_bytes(T, h), "bwd_dropout": spr.dropout_workspace_bytes(T, h)},
         "fwd_bwd_hbm_gbs": (fb + bb) / (kernel_us * 1e-6) / 1e9,
         "fwd_bwd_pct_of_peak": 100 * (fb + bb) / (kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "algorithmic_bytes": {"fwd": fb, "bwd": bb, "bwd_dropout": bwd_dropout_bytes(w, T)},
@@ -411,6 +440,9 @@ def main():
     ap.add_argument("--slabs", choices=("recommended", "contiguous"), default="recommended",
                     help="partial-slab layout: sp_region_partials_stride, or back to back (stride T*h)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the p = 0 forward and the warm one-set passes (they launch the step's kernels "
+                         "again, so a profiler's per-kernel averages would mix them in)")
     ap.add_argument("--summarize-rocprof", metavar="DIR")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()

@@ -10,8 +10,11 @@
 // the same section): dpartial = dx * keep * scale with the forward's own
 // mask, the gradient of every slab, and dbias_j = sum_i dpartial_ij.
 //
-// Stage 1 (sp_region_bwd_rows_kernel): G blocks, block b owns the contiguous
-// rows [b*T/G, (b+1)*T/G).  Each thread owns a fixed set of columns, keeps
+// Stage 1 (sp_region_bwd_rows_kernel): G blocks, block b owns rows b, b + G,
+// b + 2G, ... (interleaved, so the rows the G blocks read at one moment form
+// one contiguous band of memory; contiguous runs of T/G rows per block put
+// the concurrent reads T/G rows apart, a power-of-two stride at the usual
+// shapes, which measured 2-9% slower).  Each thread owns a fixed set of columns, keeps
 // their gamma and their dgamma/dbeta (/dbias) running sums in registers
 // across rows, and the block writes one float32 partial per gradient to the
 // workspace.  Rows stream through a ring of RING packed row buffers (RING
@@ -70,8 +73,12 @@ __device__ __forceinline__ void rows_stage(const BwdParams& p) {
   const int lane = tid & (kWave - 1), wave = tid / kWave, nwaves = bs / kWave;
   const int h = p.h;
   const int nvec = h / V;
-  const int r0 = static_cast<int>(static_cast<int64_t>(blockIdx.x) * p.T / p.G);
-  const int r1 = static_cast<int>(static_cast<int64_t>(blockIdx.x + 1) * p.T / p.G);
+  // Local row li of this block is global row blockIdx.x + li*G (G <= T, so
+  // every block has at least one row).
+  const int r0 = 0;
+  const int r1 = static_cast<int>((p.T - blockIdx.x + p.G - 1) / p.G);
+  const int bx = blockIdx.x, G = p.G;
+  auto grow = [=](int li) { return bx + li * G; };
   const bool ln = p.norm == 0;
   const float inv_h = 1.0f / static_cast<float>(h);
 
@@ -102,7 +109,7 @@ __device__ __forceinline__ void rows_stage(const BwdParams& p) {
   const char* stand_in = static_cast<const char*>(p.gamma);
   auto issue = [&](RowBuf<VPT, DRES>& b, int row) {
     const bool live = row < r1;   // block-uniform
-    const int64_t off = static_cast<int64_t>(row) * h * EB;
+    const int64_t off = static_cast<int64_t>(grow(row)) * h * EB;
     const char* dyp = live ? static_cast<const char*>(p.dy) + off : stand_in;
     const char* zp = live ? static_cast<const char*>(p.z) + off : stand_in;
     const char* drp = DRES && live ? static_cast<const char*>(p.dres) + off : stand_in;
@@ -112,7 +119,7 @@ __device__ __forceinline__ void rows_stage(const BwdParams& p) {
       b.z[k] = ld16_stream(zp + vv[k] * 16);
       if constexpr (DRES) b.dr[k] = ld16_stream(drp + vv[k] * 16);
     }
-    const int srow = live ? row : r1 - 1;
+    const int srow = grow(live ? row : r1 - 1);
     b.mu = ln ? p.mean[srow] : 0.0f;
     b.rs = p.rstd[srow];
     if constexpr (DROP) {
@@ -164,7 +171,7 @@ __device__ __forceinline__ void rows_stage(const BwdParams& p) {
     }
     const float c1 = ln ? s1 * inv_h : 0.0f;
     const float c2 = s2 * inv_h;
-    const int64_t off = static_cast<int64_t>(row) * h * EB;
+    const int64_t off = static_cast<int64_t>(grow(row)) * h * EB;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       if (!valid[k]) continue;
