@@ -162,6 +162,48 @@ def cpu_baseline(w, inp, budget_s=12.0, chunk=64):
                        f"{el:.1f} s, single process: numpy element-wise ops on one core)")
 
 
+def _cpu_worker(args):
+    """One process of the token-partitioned oracle baseline: rows [r0, r1) of
+    the shard, cycled in chunks, for budget_s seconds.  Returns (rows, s)."""
+    name, r0, r1, budget_s, chunk = args
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import numpy as np
+    import oracle.region as ref
+    import workloads as W
+    w = W.BY_NAME[name]
+    inp = W.make_inputs(w)
+    done, start, t0 = 0, r0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        rows = np.arange(start, min(r1, start + chunk))
+        o = ref.region_forward(inp["partials"], t=w.t, rank=0, dtype=w.dtype, norm=w.norm, eps=w.eps,
+                               p_drop=w.p_drop, seed=inp["seed"], gamma=inp["gamma"], beta=inp["beta"],
+                               bias=inp["bias"], residual=inp["residual"], cu_seqlens=inp["cu_seqlens"], rows=rows)
+        ref.region_backward(inp["dy"][rows], o["z"], inp["gamma"], dtype=w.dtype, norm=w.norm, eps=w.eps)
+        done += len(rows)
+        start = start + chunk if start + chunk < r1 else r0
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline_parallel(w, T, budget_s=12.0, chunk=64, max_procs=16):
+    """The same oracle, token-partitioned over one process per host core (at
+    most 16): rows are independent, so process k takes the k-th contiguous
+    share of the shard.  Processes are spawned (a fresh interpreter each),
+    never forked from this GPU-using process.  Throughput = all rows done /
+    the longest process's time.  The parameter-gradient sums are not combined
+    across processes (a fixed-order sum of a few [h] vectors)."""
+    import multiprocessing as mp
+    n = max(1, min(max_procs, len(os.sched_getaffinity(0)), T))
+    shares = [(w.name, k * T // n, (k + 1) * T // n, budget_s, chunk) for k in range(n)]
+    with mp.get_context("spawn").Pool(n) as pool:
+        res = pool.map(_cpu_worker, shares)
+    done = sum(r[0] for r in res)
+    el = max(r[1] for r in res)
+    return dict(value=done / el, unit="tokens/s", cores=n, kind="oracle",
+                sample=f"{done} rows of the {T}-row shard over {n} spawned processes, each cycling its own "
+                       f"contiguous share in chunks of {chunk} (forward + backward, {el:.1f} s)")
+
+
 # ---------------------------------------------------------------------------
 def run(args):
     import numpy as np
@@ -323,6 +365,7 @@ def run(args):
     plan = plan_timing(W)
     traffic = read_traffic()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp)
+    cpu_par = None if args.no_cpu_baseline else cpu_baseline_parallel(w, T)
     kernel_us = (fwd_ms.mean() + bwd_ms.mean()) * 1e3
     rec = {
         "metric": METRIC,
@@ -356,6 +399,7 @@ def run(args):
         "roofline": {"kernel": "sp_region_fwd_kernel", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "cpu_baseline": cpu,
+        "cpu_baseline_parallel": cpu_par,
         "host_planning": plan,
     }
     print(json.dumps(rec), flush=True)
