@@ -142,6 +142,17 @@ def plan_timing(W, n=1024, t=8, reps=200):
             "oracle_us_per_batch": oracle_us}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, budget_s=12.0, chunk=64):
     import numpy as np
     import oracle.region as ref
@@ -157,7 +168,8 @@ def cpu_baseline(w, inp, budget_s=12.0, chunk=64):
         done += len(rows)
         start = (start + chunk) % T
     el = time.perf_counter() - t0
-    return dict(value=done / el, unit="tokens/s", cores=1, kind="oracle",
+    return dict(value=done / el, unit="tokens/s", cores=1, kind="oracle", cpu=cpu_model(),
+                gbs=done / el * (fwd_bytes(w, T) + bwd_bytes(w, T)) / T / 1e9,
                 sample=f"{done} rows of the {T}-row shard, cycled in chunks of {chunk} (forward + backward, "
                        f"{el:.1f} s, single process: numpy element-wise ops on one core)")
 
@@ -199,7 +211,8 @@ def cpu_baseline_parallel(w, T, budget_s=12.0, chunk=64, max_procs=16):
         res = pool.map(_cpu_worker, shares)
     done = sum(r[0] for r in res)
     el = max(r[1] for r in res)
-    return dict(value=done / el, unit="tokens/s", cores=n, kind="oracle",
+    return dict(value=done / el, unit="tokens/s", cores=n, kind="oracle", cpu=cpu_model(),
+                gbs=done / el * (fwd_bytes(w, T) + bwd_bytes(w, T)) / T / 1e9,
                 sample=f"{done} rows of the {T}-row shard over {n} spawned processes, each cycling its own "
                        f"contiguous share in chunks of {chunk} (forward + backward, {el:.1f} s)")
 
