@@ -363,8 +363,30 @@ def run(args):
     if not args.no_extras:
         f0, b0, _ = timestamped_steps(p_drop=0.0)
         fw, bw, _ = timestamped_steps(rotate=False)
+        # The rotation of steps captured once in a HIP graph and replayed: the
+        # same kernels with no per-launch host work.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(len(sets)):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(len(sets)):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // len(sets))
+        t2 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_step_us = (time.perf_counter() - t2) / (reps * len(sets)) * 1e6
+        del graph
         extras = {"p0_step_us": {"fwd": float(f0.mean() * 1e3), "bwd": float(b0.mean() * 1e3)},
-                  "warm_one_set_step_us": {"fwd": float(fw.mean() * 1e3), "bwd": float(bw.mean() * 1e3)}}
+                  "warm_one_set_step_us": {"fwd": float(fw.mean() * 1e3), "bwd": float(bw.mean() * 1e3)},
+                  "graph_replay_step_us": graph_step_us}
 
     fb, bb = fwd_bytes(w, T), bwd_bytes(w, T)
     fwd_s = float(fwd_ms.mean()) * 1e-3
