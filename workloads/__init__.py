@@ -193,3 +193,18 @@ def as_torch(a: Optional[np.ndarray], device):
     if a.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def device_normal(shape, *, seed: int, device, scale: float = 1.0, dtype=None):
+    """Seeded N(0, scale^2) draws generated on ``device`` (torch's Philox
+    generator), stored in ``dtype`` (default bfloat16): the inputs of shards too
+    large to draw on the host.  The values are fixed by (seed, shape, device
+    type); tests copy back only the rows they check.  Drawn in float32 one
+    leading index at a time, so the float32 staging stays one slice."""
+    import torch
+    dtype = torch.bfloat16 if dtype is None else dtype
+    g = torch.Generator(device=device).manual_seed(seed)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    for i in range(shape[0]):
+        out[i] = (torch.randn(shape[1:], generator=g, device=device, dtype=torch.float32) * scale).to(dtype)
+    return out
