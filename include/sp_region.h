@@ -169,7 +169,8 @@ int sp_region_fwd_slabs(int64_t b, int64_t s, int64_t h, int32_t t, float eps, f
 
 /*
  * Bytes of device workspace sp_region_bwd needs for n_local_tokens = T rows of
- * h channels: float32 dgamma/dbeta partial sums of G = min(T, 256) row blocks,
+ * h channels: float32 dgamma/dbeta partial sums of G = min(ceil(T/4), 256) row
+ * blocks (at least 4 rows per block on shards of fewer than 1024 rows),
  * two slots of h per block.  Slots and blocks sit at strides 1 KiB past a
  * multiple of 2 KiB (slot: round_up(h, 512) + 256 floats; block:
  * round_up(2*slot, 512) + 256 floats), so the blocks' simultaneous partial

@@ -99,7 +99,13 @@ struct BwdParams {
 #define SPR_BWD_BLOCKS 256
 #endif
 constexpr int kBwdMaxBlocks = SPR_BWD_BLOCKS;
-inline int64_t bwd_blocks(int64_t T, int64_t /*h*/) { return T < kBwdMaxBlocks ? T : kBwdMaxBlocks; }
+#ifndef SPR_BWD_MIN_ROWS
+#define SPR_BWD_MIN_ROWS 4   // rows per row block on small shards (page_demo backward 16.6 -> 15.8 us)
+#endif
+inline int64_t bwd_blocks(int64_t T, int64_t /*h*/) {
+  const int64_t g = (T + SPR_BWD_MIN_ROWS - 1) / SPR_BWD_MIN_ROWS;
+  return g < kBwdMaxBlocks ? g : kBwdMaxBlocks;
+}
 
 // Workspace layout of the backward's partials (floats): slot j of block b at
 // b*ws_block_stride(h, nslots) + j*ws_slot_stride(h).  Both strides are 1 KiB

@@ -74,8 +74,10 @@ def test_workspace_bytes_is_pure(lib):
     # two slots per block at strides 1 KiB past a multiple of 2 KiB (floats: slot
     # round_up(h, 512) + 256, block round_up(2 * slot, 512) + 256), 256 blocks
     assert ws(2048, 8192) == 256 * (2 * (8192 + 256) + 256) * 4
-    assert ws(64, 512) == 64 * (2 * (512 + 256) + 256) * 4        # T < 256: one row per block
-    assert ws(10, 520) == 10 * (2560 + 256) * 4                  # slot 1024 + 256 floats; 2 slots 2560 -> + 256
+    # G = min(ceil(T / 4), 256) row blocks: at least 4 rows per block on small shards
+    assert ws(64, 512) == 16 * (2 * (512 + 256) + 256) * 4
+    assert ws(10, 520) == 3 * (2560 + 256) * 4                   # slot 1024 + 256 floats; 2 slots 2560 -> + 256
+    assert ws(1, 8) == 1 * (2 * (512 + 256) + 256) * 4 and ws(1024, 8) == ws(4096, 8) == 256 * 1792 * 4
     assert ws(16384, 8192) == ws(2048, 8192)
 
 
@@ -166,10 +168,10 @@ def test_fwd_empty_shard_is_noop(lib):
     assert call_fwd(lib, a) == spr.SPR_OK
 
 
-# Workspace bytes of the T = 64, h = 512 backward cases: 64 blocks, slots of
+# Workspace bytes of the T = 64, h = 512 backward cases: 16 blocks, slots of
 # 512 + 256 floats, blocks of round_up(nslots * 768, 512) + 256 floats.
-WS2 = 64 * (1536 + 256) * 4
-WS3 = 64 * (2560 + 256) * 4
+WS2 = 16 * (1536 + 256) * 4
+WS3 = 16 * (2560 + 256) * 4
 
 
 def bwd_args(**over):
@@ -235,7 +237,7 @@ def test_bwd_dropout_workspace_bytes(lib):
     assert ws3(0, 64) == 0 and ws3(5, 0) == 0
     for T, h in [(64, 512), (2048, 8192), (100000, 5120), (1, 8)]:
         slot = (h + 511) // 512 * 512 + 256
-        blocks = min(T, 256)
+        blocks = min((T + 3) // 4, 256)
         assert ws2(T, h) == blocks * ((2 * slot + 511) // 512 * 512 + 256) * 4
         assert ws3(T, h) == blocks * ((3 * slot + 511) // 512 * 512 + 256) * 4
 
