@@ -207,8 +207,13 @@ def cpu_baseline_parallel(w, T, budget_s=12.0, chunk=64, max_procs=16):
     import multiprocessing as mp
     n = max(1, min(max_procs, len(os.sched_getaffinity(0)), T))
     shares = [(w.name, k * T // n, (k + 1) * T // n, budget_s, chunk) for k in range(n)]
-    with mp.get_context("spawn").Pool(n) as pool:
+    pool = mp.get_context("spawn").Pool(n)
+    try:
         res = pool.map(_cpu_worker, shares)
+        pool.close()          # no more work: the workers exit on their own
+    finally:
+        pool.terminate()      # no-op after close(); ends them on an exception
+        pool.join()           # every worker (and the pool's threads) gone before returning
     done = sum(r[0] for r in res)
     el = max(r[1] for r in res)
     return dict(value=done / el, unit="tokens/s", cores=n, kind="oracle", cpu=cpu_model(),

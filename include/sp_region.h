@@ -180,7 +180,11 @@ int sp_region_fwd_slabs(int64_t b, int64_t s, int64_t h, int32_t t, float eps, f
 size_t sp_region_bwd_workspace_bytes(int64_t n_local_tokens, int64_t h);
 
 /*
- * Backward of the normalisation (the adjoint of the forward's last step).
+ * Backward of the normalisation (the adjoint of the forward's last step):
+ * hpc.payai.win lesson 7 "Sequence parallelism", section 3.B (the backward of
+ * each forward step is its adjoint, computed on the same s/t token slice),
+ * applied to the LayerNorm of section 2 (mean and population variance over
+ * the full h, eps inside the square root) and to RMSNorm.
  *
  *   b, s, t, h, norm, dtype   as in sp_region_fwd (T = b*s/t).
  *   gamma        [h].

@@ -465,18 +465,22 @@ def _autograd_function():
     import torch
 
     class SPRegion(torch.autograd.Function):
-        """(partials [t][T][h], gamma, beta, bias, residual) -> (y, z).
+        """(gamma, beta, bias, residual, cfg, *slabs) -> (y, z).  The slabs are
+        one [t][T][h] tensor, or t separate [T][h] tensors (cfg["slab_list"]).
 
         Backward: y's gradient is dy, z's gradient (z is also the next
-        residual stream) is dres_in; returns the gradients of the slabs (the
-        same dpartial for every slab), gamma, beta, bias and residual."""
+        residual stream) is dres_in; returns the gradients of gamma, beta,
+        bias and residual, then of the slabs (the same dpartial for every
+        slab)."""
 
         @staticmethod
-        def forward(ctx, partials, gamma, beta, bias, residual, cfg):
-            o = fwd(partials, gamma, beta, bias=bias, residual=residual, **cfg)
+        def forward(ctx, gamma, beta, bias, residual, cfg, *slabs):
+            fcfg = {k: v for k, v in cfg.items() if k != "slab_list"}
+            partials = list(slabs) if cfg["slab_list"] else slabs[0]
+            o = fwd(partials, gamma, beta, bias=bias, residual=residual, **fcfg)
             ctx.save_for_backward(o.z, o.mean, o.rstd, gamma)
             ctx.cfg = cfg
-            ctx.shape = tuple(partials.shape)
+            ctx.shapes = [tuple(x.shape) for x in slabs]
             ctx.flags = (beta is not None, bias is not None, residual is not None)
             return o.y, o.z
 
@@ -490,9 +494,13 @@ def _autograd_function():
                             p_drop=cfg["p_drop"], seed=cfg["seed"], norm=cfg.get("norm", "layernorm"),
                             cu_seqlens=cfg.get("cu_seqlens"), dres_in=None if dz is None else dz.contiguous(),
                             want_dbeta=has_beta, want_dbias=has_bias)
-            dpart = g.dpartial.unsqueeze(0).expand(ctx.shape)
-            return (dpart, g.dgamma.to(gamma.dtype), None if g.dbeta is None else g.dbeta.to(gamma.dtype),
-                    None if g.dbias is None else g.dbias.to(gamma.dtype), g.dx if has_res else None, None)
+            if cfg["slab_list"]:
+                dslabs = tuple(g.dpartial for _ in ctx.shapes)
+            else:
+                dslabs = (g.dpartial.unsqueeze(0).expand(ctx.shapes[0]),)
+            return (g.dgamma.to(gamma.dtype), None if g.dbeta is None else g.dbeta.to(gamma.dtype),
+                    None if g.dbias is None else g.dbias.to(gamma.dtype), g.dx if has_res else None,
+                    None) + dslabs
 
     return SPRegion
 
@@ -503,10 +511,15 @@ _SPREGION = None
 def region(partials, gamma, beta=None, *, bias=None, residual=None, b: int, s: int, t: int, rank: int,
            eps: float, p_drop: float, seed: int, norm: Union[str, int] = "layernorm", cu_seqlens=None):
     """Autograd-aware region: returns (y, z); gradients flow to partials (every
-    slab receives dpartial), gamma, beta, bias and residual.  dgamma, dbeta
-    and dbias are computed in float32 and returned in the parameters' dtype."""
+    slab receives dpartial), gamma, beta, bias and residual.  partials is one
+    [t][T][h] tensor or a list of t [T][h] tensors (each then receives its
+    own gradient).  dgamma, dbeta and dbias are computed in float32 and
+    returned in the parameters' dtype."""
     global _SPREGION
     if _SPREGION is None:
         _SPREGION = _autograd_function()
-    cfg = dict(b=b, s=s, t=t, rank=rank, eps=eps, p_drop=p_drop, seed=seed, norm=norm, cu_seqlens=cu_seqlens)
-    return _SPREGION.apply(partials, gamma, beta, bias, residual, cfg)
+    slab_list = isinstance(partials, (list, tuple))
+    slabs = tuple(partials) if slab_list else (partials,)
+    cfg = dict(b=b, s=s, t=t, rank=rank, eps=eps, p_drop=p_drop, seed=seed, norm=norm, cu_seqlens=cu_seqlens,
+               slab_list=slab_list)
+    return _SPREGION.apply(gamma, beta, bias, residual, cfg, *slabs)

@@ -1,24 +1,18 @@
 """Analytic memory and communication model of Megatron TP+SP (test infrastructure only).
 
 Source: hpc.payai.win lesson 7 "Sequence parallelism".
-  * Code exercise and its answer: a block is traced through the regions
-    layernorm -> col_linear -> gelu -> row_linear -> dropout, tracking the
-    activation shape (s, h).  Without SP every region sees the full sequence;
-    the column-parallel linear splits h by tp, the row-parallel linear restores
-    it.  With SP the layernorm and dropout regions hold s/tp tokens; an
-    all-gather (g) restores the full sequence before the column-parallel linear
-    and a reduce-scatter (g*) cuts the row-parallel output back to s/tp.  The
-    g / row-output / g* buffers are transient; every region's own activation is
-    stored for the backward.  The peak stored activation in bf16 is
-    max(b*s*h*2) over stored entries.
+  * Code exercise (shape trace) and its answer: the activation shapes of one
+    block's regions with and without SP, which tensors are kept for the
+    backward and which are communication buffers, and the peak kept
+    activation in bf16 (printed: 33.6 MB without SP, 4.2 MB with SP at
+    s = h = 4096, t = 8).  Modelled below as a per-region sharding table plus
+    separate boundary and stored-for-backward rules.
   * Section 4: ring all-reduce = reduce-scatter then all-gather; per rank
     V_AR = 2(t-1)/t * Size and V_RS = V_AG = (t-1)/t * Size; a block moves
     2 all-reduces without SP and 2 all-gathers + 2 reduce-scatters with SP,
     both 4(t-1)/t * (2bsh) bytes.
-  * Worked example: per-layer activations sbh(10 + 24/t + 5as/(ht)) bytes,
-    whose non-TP part is about 10sbh (two LayerNorm inputs 4sbh, the inputs of
-    the QKV projection and the first MLP linear 4sbh, two 1-byte dropout masks
-    2sbh); SP divides that part by t.
+  * Worked example (70B model): the non-TP part of the per-layer stored
+    activations is about 10sbh bytes, and SP divides it by t.
 """
 from __future__ import annotations
 
@@ -27,62 +21,84 @@ from typing import List, Tuple
 
 import numpy as np
 
-TraceEntry = Tuple[str, int, int, bool]   # (region, s, h, stored_for_backward)
+Tensor = Tuple[str, int, int, bool]   # (label, s, h, kept for the backward)
 
-REGIONS = ("layernorm", "col_linear", "gelu", "row_linear", "dropout")
+# The regions one block's forward passes through, in order (the lesson's code
+# exercise traces these five).  Each region is described by which axis the
+# tensor-parallel degree divides in its output, with sequence parallelism on
+# and off.  Token-wise ops (LayerNorm, dropout) sit in the non-TP region:
+# sequence parallelism gives every rank s/t of the tokens with all h channels
+# (section 2 and section 3), and without it they hold the whole (s, h).  The
+# column-parallel linear divides the hidden axis, the activation after it is
+# element-wise, and the row-parallel linear's output has the full (s, h) again.
+BLOCK = ("layernorm", "col_linear", "gelu", "row_linear", "dropout")
+SPLIT_AXIS = {            # region: (axis divided by t with SP, axis divided by t without SP)
+    "layernorm": ("s", None),
+    "col_linear": ("h", "h"),
+    "gelu": ("h", "h"),
+    "row_linear": (None, None),
+    "dropout": ("s", None),
+}
+
+# With SP the block crosses the SP/TP boundary twice (section 3.A): the
+# all-gather g restores the whole sequence before the column-parallel
+# linear, and after the row-parallel linear its full-h output is reduced and
+# cut back to the rank's s/t tokens by the reduce-scatter g*.  Those tensors
+# are communication or temporary buffers: (position, region, label, axis
+# divided by t).
+BOUNDARY = (
+    ("before", "col_linear", "g_all_gather", None),
+    ("after", "row_linear", "row_out", None),
+    ("after", "row_linear", "g_star_reduce_scatter", "s"),
+)
 
 
-def trace_block(seq: int, hidden: int, tp: int, enable_sp: bool) -> List[TraceEntry]:
-    """Activation shapes of one block's forward, in region order."""
-    out: List[TraceEntry] = []
-    s_full, h_full = seq, hidden
-    s_sp = seq // tp if enable_sp else seq          # sequence length inside the SP region
-    for region in REGIONS:
-        if region == "layernorm":
-            out.append((region, s_sp, h_full, True))
-        elif region == "col_linear":
-            if enable_sp:                             # g: all-gather along s into the TP region
-                out.append(("g_all_gather", s_full, h_full, False))
-            out.append((region, s_full, h_full // tp, True))
-        elif region == "gelu":
-            out.append((region, s_full, h_full // tp, True))
-        elif region == "row_linear":
-            # Without SP the all-reduced row output is the next region's stored input.
-            # With SP it is a partial sum, transient until g* reduces and splits it.
-            out.append((region, s_full, h_full, not enable_sp))
-            if enable_sp:
-                out.append(("row_out", s_full, h_full, False))
-                out.append(("g_star_reduce_scatter", s_sp, h_full, False))
-        elif region == "dropout":
-            out.append((region, s_sp, h_full, True))
+def _kept(region: str, sp: bool) -> bool:
+    """Stored-for-backward rule: every region's output is kept, except the
+    row-parallel linear's under SP, which is a partial sum that only lives
+    until g* reduces it (its backward needs the region's input instead)."""
+    return not (sp and region == "row_linear")
+
+
+def _shape(axis, seq: int, hidden: int, tp: int) -> Tuple[int, int]:
+    return (seq // tp, hidden) if axis == "s" else (seq, hidden // tp) if axis == "h" else (seq, hidden)
+
+
+def shape_trace(seq: int, hidden: int, tp: int, sp: bool) -> List[Tensor]:
+    """Activation tensors of one block's forward, in creation order:
+    (label, s, h, kept).  Boundary buffers exist only with SP and are never kept."""
+    out: List[Tensor] = []
+    for region in BLOCK:
+        if sp:
+            out += [(lab, *_shape(ax, seq, hidden, tp), False)
+                    for pos, reg, lab, ax in BOUNDARY if pos == "before" and reg == region]
+        axis = SPLIT_AXIS[region][0 if sp else 1]
+        out.append((region, *_shape(axis, seq, hidden, tp), _kept(region, sp)))
+        if sp:
+            out += [(lab, *_shape(ax, seq, hidden, tp), False)
+                    for pos, reg, lab, ax in BOUNDARY if pos == "after" and reg == region]
     return out
 
 
-def bf16_bytes(s: int, h: int, batch: int = 1) -> int:
-    return batch * s * h * 2
-
-
-def max_stored_bytes(trace: List[TraceEntry], batch: int = 1) -> int:
-    """Peak stored (kept for backward) activation in bf16 bytes."""
-    return max(bf16_bytes(s, h, batch) for _, s, h, stored in trace if stored)
+def max_stored_bytes(trace: List[Tensor], batch: int = 1) -> int:
+    """Peak kept activation: the largest kept tensor, at 2 bytes (bf16) per
+    element of batch * s * h."""
+    return max(2 * batch * s * h for _, s, h, kept in trace if kept)
 
 
 def nontp_activation_bytes(s: int, b: int, h: int, t: int, sp: bool) -> Fraction:
-    """The non-TP part of the per-layer stored activations: 10*s*b*h bytes,
-    divided by t under SP.  Returned exactly as a Fraction."""
+    """The non-TP part of the per-layer stored activations of the 70B worked
+    example: 10*s*b*h bytes (two LayerNorm inputs, the inputs of the QKV
+    projection and of the first MLP linear, all bf16, and two one-byte
+    dropout masks), divided by t under SP.  Returned exactly as a Fraction.
+    (The worked example evaluates only this part of the per-layer formula;
+    the formula's attention term needs the head count, which the example
+    never gives, so it is not modelled here.)"""
     ln_inputs = 2 * (s * b * h) * 2          # two LayerNorm inputs, bf16
     gemm_inputs = 2 * (s * b * h) * 2        # QKV projection and MLP first-linear inputs
     dropout_masks = 2 * (s * b * h) * 1      # two dropout masks, one byte per element
     total = Fraction(ln_inputs + gemm_inputs + dropout_masks)
     return total / t if sp else total
-
-
-def activation_bytes_per_layer(s: int, b: int, h: int, t: int, a: int, sp: bool) -> Fraction:
-    """sbh(10 + 24/t + 5as/(ht)) without SP; the 10sbh term divided by t with SP.
-    Exact (Fraction).  The head count a is a free parameter."""
-    sbh = Fraction(s * b * h)
-    tp_part = sbh * (Fraction(24, t) + Fraction(5 * a * s, h * t))
-    return nontp_activation_bytes(s, b, h, t, sp) + tp_part
 
 
 def comm_volume(t: int, size: int) -> dict:

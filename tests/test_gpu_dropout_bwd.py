@@ -147,12 +147,13 @@ def test_planned_buckets_end_to_end(cuda_device):
     assert ran >= 2
 
 
-@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
-def test_autograd_region_matches_torch_autograd(cuda_device, norm):
+@pytest.mark.parametrize("norm,slab_list", [("layernorm", False), ("rmsnorm", False), ("layernorm", True)])
+def test_autograd_region_matches_torch_autograd(cuda_device, norm, slab_list):
     """spr.region under torch.autograd: the gradients of slabs, gamma, beta,
     bias and residual for loss = sum(y*gy) + sum(z*gz) against torch's own
     autograd in float64 on the CPU through the same forward (the oracle's
-    keep mask, float32 scale)."""
+    keep mask, float32 scale).  slab_list: the slabs as t separate leaf
+    tensors, each of which must receive its own gradient."""
     import torch
     import torch.nn.functional as F
     T, h, t, p, eps, seed = 24, 256, 3, 0.3, 1e-5, 0x1234
@@ -180,10 +181,14 @@ def test_autograd_region_matches_torch_autograd(cuda_device, norm):
 
     g = lambda a: None if a is None else torch.from_numpy(a).to(cuda_device).requires_grad_(True)
     Pg, gg, bg, biasg, rg = g(P), g(gamma), g(beta), g(bias), g(res)
-    yg, zg = spr.region(Pg, gg, bg, bias=biasg, residual=rg, b=1, s=t * T, t=t, rank=1, eps=eps, p_drop=p,
-                        seed=seed, norm=norm)
+    slabs = [g(np.ascontiguousarray(P[k])) for k in range(t)] if slab_list else None
+    yg, zg = spr.region(slabs if slab_list else Pg, gg, bg, bias=biasg, residual=rg, b=1, s=t * T, t=t, rank=1,
+                        eps=eps, p_drop=p, seed=seed, norm=norm)
     (yg * torch.from_numpy(gy).to(cuda_device)).sum().add((zg * torch.from_numpy(gz).to(cuda_device)).sum()).backward()
     torch.cuda.synchronize()
+    if slab_list:
+        assert Pg.grad is None
+        Pg = type("Grads", (), {"grad": torch.stack([sk.grad for sk in slabs])})()
     for name, a, b in [("slabs", Pg, Pc), ("gamma", gg, gc), ("beta", bg, bc), ("bias", biasg, biasc),
                        ("residual", rg, rc)]:
         if a is None:

@@ -7,9 +7,8 @@ from fractions import Fraction
 import numpy as np
 from hypothesis import given, settings, strategies as st
 
-from oracle.analytic import (activation_bytes_per_layer, comm_volume, max_stored_bytes,
-                             nontp_activation_bytes, ring_all_gather, ring_reduce_scatter,
-                             trace_block)
+from oracle.analytic import (comm_volume, max_stored_bytes, nontp_activation_bytes, ring_all_gather,
+                             ring_reduce_scatter, shape_trace)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -22,8 +21,8 @@ def load(name):
 def test_trace_answer_printed_values():
     g = load("lesson7_trace_answer.json")
     i, p = g["inputs"], g["printed"]
-    tp_only = trace_block(i["seq"], i["hidden"], i["tp"], enable_sp=False)
-    tp_sp = trace_block(i["seq"], i["hidden"], i["tp"], enable_sp=True)
+    tp_only = shape_trace(i["seq"], i["hidden"], i["tp"], sp=False)
+    tp_sp = shape_trace(i["seq"], i["hidden"], i["tp"], sp=True)
     m_tp, m_sp = max_stored_bytes(tp_only), max_stored_bytes(tp_sp)
     assert round(m_tp / 1e6, 1) == p["tp_only_peak_MB"]
     assert round(m_sp / 1e6, 1) == p["tp_sp_peak_MB"]
@@ -44,7 +43,7 @@ def test_trace_answer_printed_values():
 @given(st.integers(1, 64), st.integers(1, 64), st.sampled_from([1, 2, 4, 8, 16]), st.integers(1, 4))
 def test_peak_ratio_is_t(sq, hq, t, b):
     s, h = sq * t, hq * t
-    assert max_stored_bytes(trace_block(s, h, t, False), b) == t * max_stored_bytes(trace_block(s, h, t, True), b)
+    assert max_stored_bytes(shape_trace(s, h, t, False), b) == t * max_stored_bytes(shape_trace(s, h, t, True), b)
 
 
 def test_worked_example_printed_values():
@@ -64,16 +63,19 @@ def test_worked_example_printed_values():
     assert sp / tp == Fraction(*p["sp_fraction_of_tp_only"])
 
 
-def test_activation_formula_structure():
-    # The SP saving is the non-TP term only, independent of the head count a;
-    # the TP-sharded terms are identical with and without SP.  (The head count
-    # of the 70B example is not given, so the a-dependent term has no printed
-    # value to pin: only its structure is checked.)
-    s, b, h, t = 16384, 1, 8192, 8
-    for a in (1, 32, 64, 128):
-        d = activation_bytes_per_layer(s, b, h, t, a, sp=False) - activation_bytes_per_layer(s, b, h, t, a, sp=True)
-        assert d == Fraction(10 * s * b * h) * (1 - Fraction(1, t))
-    assert activation_bytes_per_layer(s, b, h, 1, 0, sp=False) == 34 * s * b * h
+def test_trace_kept_tensors_hold_every_element_once():
+    # Closed form independent of the table: the kept tensors of the TP-only
+    # block are two full (s, h) token-wise tensors, two (s, h/t) TP tensors
+    # and the all-reduced row output (s, h); with SP the token-wise tensors
+    # shrink to s/t and the row output is no longer kept.  Boundary buffers
+    # are never kept and exist only with SP.
+    for s, h, t in ((4096, 4096, 8), (96, 40, 4), (7, 5, 1)):
+        tp = shape_trace(s, h, t, sp=False)
+        sp = shape_trace(s, h, t, sp=True)
+        assert sum(sh * hh for _, sh, hh, k in tp if k) == 3 * s * h + 2 * s * (h // t)
+        assert sum(sh * hh for _, sh, hh, k in sp if k) == 2 * (s // t) * h + 2 * s * (h // t)
+        assert all(k for *_, k in tp) and len(tp) == 5
+        assert sum(1 for *_, k in sp if not k) == 4 and len(sp) == 8
 
 
 def test_comm_volume_closed_forms_and_saving():

@@ -184,6 +184,52 @@ def make_inputs(w: Workload, seed: Optional[int] = None, with_dy: bool = True) -
     return out
 
 
+def with_hard_rows(inp: Dict, *, loc: float, small: float = 0.003, gamma_range=(8.0, 16.0), dy_scale: float = 8.0,
+                   seed: int = 5) -> Dict:
+    """A copy of a drawn shard whose first four rows are numerically hard for
+    the normalisation, with large gamma and dy so that |y| and |dx| reach well
+    above 8.  The rows' z (the residual row, or slab 0's row without a
+    residual) are:
+      0  constant 1.5 (variance exactly 0);
+      1  all zero (RMSNorm: mean square exactly 0);
+      2  loc + N(0, 1) (|mean| >> std);
+      3  N(0, small^2) (variance of the order of eps).
+    With a residual, the rows' slabs are zero except slab 0 = -bias (when
+    there is a bias), so the slab sum plus bias is exactly 0 and z equals the
+    residual row whatever the dropout mask.  Without a residual the rows go
+    into slab 0 and the shard must have neither bias nor dropout.  Only values
+    are set here; nothing of the region is computed."""
+    w = inp["workload"]
+    rng = np.random.default_rng(seed)
+    T, h = inp["T"], inp["h"]
+    assert T >= 4
+    out = dict(inp)
+    P = inp["partials"].copy()
+    res = inp["residual"].copy() if inp["residual"] is not None else None
+    bias = inp["bias"]
+    if res is None:
+        assert bias is None and w.p_drop == 0.0
+    rows = {
+        0: np.full(h, 1.5),
+        1: np.zeros(h),
+        2: loc + rng.standard_normal(h),
+        3: small * rng.standard_normal(h),
+    }
+    zero = _to_storage(np.zeros(h), w.dtype)
+    for r, vals in rows.items():
+        P[:, r] = zero
+        if res is not None:
+            res[r] = _to_storage(vals, w.dtype)
+            if bias is not None:   # slab 0 = -bias: the sign bit flipped, exact in both dtypes
+                P[0, r] = (-bias) if w.dtype == DTYPE_F32 else (bias ^ np.uint16(0x8000))
+        else:
+            P[0, r] = _to_storage(vals, w.dtype)
+    out["partials"], out["residual"] = P, res
+    out["gamma"] = _to_storage(rng.uniform(*gamma_range, size=h), w.dtype)
+    out["dy"] = _draw(rng, (T, h), w.dtype, scale=dy_scale)
+    return out
+
+
 def as_torch(a: Optional[np.ndarray], device):
     """numpy storage array -> torch tensor on ``device`` (bf16 bits are viewed
     as torch.bfloat16; nothing is converted)."""
