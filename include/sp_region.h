@@ -28,7 +28,8 @@
  *   - dtype SPR_BF16: activations, gamma, beta and bias are bfloat16;
  *     SPR_F32: all float32.  mean, rstd, dgamma, dbeta are always float32.
  *   - The caller owns every buffer (the backward workspace included).  The
- *     library allocates nothing, keeps no mutable global state, launches
+ *     library allocates nothing, keeps no mutable global state (except the
+ *     static device scratch of sp_region_bwd_noalloc), launches
  *     asynchronously on `stream`, never synchronises and never reads device
  *     memory on the host.  Outputs are overwritten, not accumulated.
  *   - Errors: a nonzero status is returned BEFORE any launch and leaves every
@@ -47,14 +48,15 @@
 extern "C" {
 #endif
 
-#define SP_REGION_ABI_VERSION 2   /* 2 added sp_region_bwd_accumulate */
+#define SP_REGION_ABI_VERSION 3   /* 2 added sp_region_bwd_accumulate; 3 sp_region_bwd_noalloc */
 
 enum sp_region_status {
   SPR_OK = 0,
   SPR_ERR_INVALID_ARG = 1,  /* argument outside its documented domain */
   SPR_ERR_UNSUPPORTED = 2,  /* valid, but not compiled for (h, t, dtype) */
   SPR_ERR_ALIGNMENT = 3,    /* pointer or slab stride not 16-byte aligned */
-  SPR_ERR_HIP = 4           /* kernel launch failed (see sp_region_last_hip_error) */
+  SPR_ERR_HIP = 4,          /* kernel launch failed (see sp_region_last_hip_error) */
+  SPR_ERR_SCRATCH = 5       /* sp_region_bwd_noalloc: the shard needs more than its static scratch */
 };
 
 enum sp_region_dtype { SPR_F32 = 0, SPR_BF16 = 1 };
@@ -213,6 +215,34 @@ int sp_region_bwd(int64_t b, int64_t s, int64_t h, int32_t t,
                   void* dx, float* dgamma, float* dbeta,
                   void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/*
+ * sp_region_bwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Every argument, check and result is that of sp_region_bwd (same kernels,
+ * bit for bit the same outputs); the workspace is not passed: the partial
+ * sums live in a static device array of SPR_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on, until the process ends.  The call
+ * allocates nothing and frees nothing.
+ *
+ *   Limit: sp_region_bwd_workspace_bytes(T, h) <= SPR_NOALLOC_SCRATCH_BYTES
+ *   (32 MiB: every shard up to h = 8192, and up to 1000 rows at h = 16384),
+ *   else SPR_ERR_SCRATCH before any launch, outputs untouched.
+ *   Races: every call on one GPU uses that GPU's one array, which keeps the
+ *   last call's contents (the kernels need no particular contents on entry).
+ *   Calls that can overlap on one GPU -- on different streams, or from
+ *   different threads without ordering -- race on it and give wrong
+ *   results; order them (one stream, or events).
+ *   The array's address on the GPU that runs `stream` is looked up on the
+ *   first call there (hipGetSymbolAddress) and kept.
+ */
+#define SPR_NOALLOC_SCRATCH_BYTES (32u << 20)
+int sp_region_bwd_noalloc(int64_t b, int64_t s, int64_t h, int32_t t,
+                          const void* gamma, int32_t norm, int32_t dtype,
+                          const void* dy, const void* z, const float* mean, const float* rstd,
+                          const void* dres_in,
+                          void* dx, float* dgamma, float* dbeta,
+                          void* stream);
 
 /*
  * Bytes of device workspace sp_region_bwd_dropout needs for T rows of h

@@ -22,10 +22,11 @@ from typing import Optional, Sequence, Union
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsp_region.so")
 
-SPR_OK, SPR_ERR_INVALID_ARG, SPR_ERR_UNSUPPORTED, SPR_ERR_ALIGNMENT, SPR_ERR_HIP = range(5)
+SPR_OK, SPR_ERR_INVALID_ARG, SPR_ERR_UNSUPPORTED, SPR_ERR_ALIGNMENT, SPR_ERR_HIP, SPR_ERR_SCRATCH = range(6)
 SPR_F32, SPR_BF16 = 0, 1
 SPR_LAYERNORM, SPR_RMSNORM = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
+NOALLOC_SCRATCH_BYTES = 32 << 20     # SPR_NOALLOC_SCRATCH_BYTES
 
 # Every symbol include/sp_region.h declares, with its ctypes signature.
 _VP, _I64, _I32, _U64, _F32, _SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64,
@@ -43,6 +44,8 @@ SIGNATURES = {
     "sp_region_bwd_workspace_bytes": (_SZ, [_I64, _I64]),
     "sp_region_bwd": (ctypes.c_int, [_I64, _I64, _I64, _I32, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
                                      _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "sp_region_bwd_noalloc": (ctypes.c_int, [_I64, _I64, _I64, _I32, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
+                                             _VP, _VP, _VP, _VP]),
     "sp_region_bwd_dropout_workspace_bytes": (_SZ, [_I64, _I64]),
     "sp_region_bwd_dropout": (ctypes.c_int, [_I64, _I64, _I64, _I32, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
                                              _F32, _I32, _U64, _VP, _I32,
@@ -319,6 +322,33 @@ def bwd(dy, z, mean, rstd, gamma, *, b: int, s: int, t: int, norm: Union[str, in
                                workspace.numel(), stream)
         _check("sp_region_bwd", st)
     return BwdOut(dx, dgamma, dbeta)
+
+
+def bwd_noalloc(dy, z, mean, rstd, gamma, *, b: int, s: int, t: int, out: BwdOut,
+                norm: Union[str, int] = "layernorm", dres_in=None) -> BwdOut:
+    """sp_region_bwd_noalloc: bwd() with the library's static device scratch as
+    its workspace, for callers that cannot allocate.  Allocates nothing, so
+    the outputs come in `out` (dx, dgamma, and dbeta or None)."""
+    import torch
+    lib = load_library()
+    nc = _norm_code(norm)
+    dev, dt = z.device, z.dtype
+    dcode = _dtype_code(dt)
+    T, h = z.shape
+    if T != local_tokens(b, s, t):
+        raise ValueError(f"z holds {T} rows, expected b*s/t = {local_tokens(b, s, t)}")
+    ln = nc == SPR_LAYERNORM
+    dx, dgamma, dbeta = out
+    for x, name, dtype_, shape in ((z, "z", dt, (T, h)), (dy, "dy", dt, (T, h)), (dres_in, "dres_in", dt, (T, h)),
+                                   (gamma, "gamma", dt, (h,)), (mean, "mean", torch.float32, (T,)),
+                                   (rstd, "rstd", torch.float32, (T,)), (dx, "dx", dt, (T, h)),
+                                   (dgamma, "dgamma", torch.float32, (h,)), (dbeta, "dbeta", torch.float32, (h,))):
+        _require(x, name, dev, dtype_, shape)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.sp_region_bwd_noalloc(b, s, h, t, _ptr(gamma), nc, dcode, _ptr(dy), _ptr(z), _ptr(mean if ln else None),
+                                   _ptr(rstd), _ptr(dres_in), _ptr(dx), _ptr(dgamma), _ptr(dbeta), stream)
+    _check("sp_region_bwd_noalloc", st)
+    return out
 
 
 def dropout_workspace_bytes(T: int, h: int) -> int:

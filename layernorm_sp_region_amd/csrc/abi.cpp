@@ -1,8 +1,10 @@
 // C ABI of the SP-region library: argument validation, then dispatch to the
 // kernel launchers.  Every check runs before any HIP call, so an invalid call
 // launches nothing and leaves the outputs untouched.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "sp_region.h"
 #include "spr_internal.h"
@@ -59,6 +61,8 @@ const char* sp_region_strerror(int status) {
     case SPR_ERR_UNSUPPORTED: return "unsupported shape (t, h or dtype outside the compiled kernels)";
     case SPR_ERR_ALIGNMENT: return "pointer or slab stride not 16-byte aligned";
     case SPR_ERR_HIP: return "HIP launch error (see sp_region_last_hip_error)";
+    case SPR_ERR_SCRATCH:
+      return "shard needs more workspace than sp_region_bwd_noalloc's static scratch (SPR_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -352,3 +356,74 @@ int sp_region_hbm_copy(const void* src, void* dst, size_t nbytes, void* stream) 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free backward.  Its workspace is this file-scope device array,
+// one copy per GPU.  In host code `scratch` names a host-side stand-in, not
+// the GPU's copy, so it is never passed to a kernel or a copy: the GPU's
+// address is looked up once per device with hipGetSymbolAddress (with that
+// device current) and kept in g_scratch.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SPR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Address of `scratch` on the GPU that runs `stream` (the current device for
+// the null stream).
+int scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_status(e);
+  int dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return SPR_ERR_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      const hipError_t e2 = dev != cur ? hipSetDevice(cur) : hipSuccess;
+      if (e != hipSuccess) return hip_status(e);
+      if (e2 != hipSuccess) return hip_status(e2);
+      if (p == nullptr) return SPR_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SPR_OK;
+}
+
+}  // namespace
+
+extern "C" int sp_region_bwd_noalloc(int64_t b, int64_t s, int64_t h, int32_t t,
+                                     const void* gamma, int32_t norm, int32_t dtype,
+                                     const void* dy, const void* z, const float* mean, const float* rstd,
+                                     const void* dres_in,
+                                     void* dx, float* dgamma, float* dbeta,
+                                     void* stream) {
+  ClearLaunchEvents clear_hook;
+  int64_t T = 0;
+  int st = check_shape(b, s, h, t, norm, dtype, &T);
+  if (st != SPR_OK) return st;
+  if (sp_region_bwd_workspace_bytes(T, h) > SPR_NOALLOC_SCRATCH_BYTES) return SPR_ERR_SCRATCH;
+  // Every argument check first, against an aligned stand-in for the scratch
+  // address; the real address replaces it once the call is known valid.
+  spr::BwdParams p;
+  st = prepare_bwd(b, s, h, t, gamma, norm, dtype, dy, z, mean, rstd, dres_in, dx, dgamma, dbeta,
+                   reinterpret_cast<void*>(uintptr_t{256}), SPR_NOALLOC_SCRATCH_BYTES, false, &p);
+  if (st != SPR_OK) return st;
+  void* ws = nullptr;
+  st = scratch_for_stream(static_cast<hipStream_t>(stream), &ws);
+  if (st != SPR_OK) return st;
+  p.ws = static_cast<float*>(ws);
+  return hip_status(spr::launch_bwd(p, dtype, static_cast<hipStream_t>(stream)));
+}
