@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SP_REGION_ABI_VERSION 3   /* 2 added sp_region_bwd_accumulate; 3 sp_region_bwd_noalloc */
+#define SP_REGION_ABI_VERSION 4   /* 2 sp_region_bwd_accumulate; 3 sp_region_bwd_noalloc; 4 sp_region_set_bwd_launches */
 
 enum sp_region_status {
   SPR_OK = 0,
@@ -203,10 +203,18 @@ size_t sp_region_bwd_workspace_bytes(int64_t n_local_tokens, int64_t h);
  *   dbeta        out float32 [h] or NULL: sum over the T rows of dy
  *                (must be NULL for RMSNorm).
  *   workspace    >= sp_region_bwd_workspace_bytes(T, h) bytes, 16-byte aligned
- *                (may be NULL when that is 0).  Contents are scratch.
+ *                (may be NULL when that is 0).  Contents on entry do not
+ *                matter; calls that share a workspace must be ordered.
  *
- * dgamma/dbeta are reduced in a fixed order, so results are bitwise
- * reproducible for a given (T, h).  T == 0 writes zeros to dgamma/dbeta.
+ * dgamma/dbeta are reduced in one fixed order (row block b = rows b, b + G,
+ * ... in order; 32 groups of blocks g, g + 32, ... in order; the groups in
+ * order), so results are bitwise reproducible for a given (T, h), whichever
+ * launch path runs.  Small shards (at most 4 rows per row block, G <= 128,
+ * and the row and column blocks together no more than the device's compute
+ * units: T <= 512 at h = 4096) take one kernel launch, in which column blocks
+ * sum dgamma/dbeta from dy and z themselves and the workspace is not used;
+ * otherwise the row blocks write partial sums to the workspace and a second
+ * launch reduces them.  T == 0 writes zeros to dgamma/dbeta.
  */
 int sp_region_bwd(int64_t b, int64_t s, int64_t h, int32_t t,
                   const void* gamma, int32_t norm, int32_t dtype,
@@ -380,6 +388,16 @@ int sp_region_sp_gate(const int32_t* lengths, int32_t n, double rs_wait_share, i
  */
 int sp_region_shard_layout(const int32_t* lengths, int32_t n, int32_t t, int32_t* padded, int32_t* cu_local,
                            int64_t* n_local_tokens);
+
+/*
+ * Launch path of the backward calls (sp_region_bwd and its accumulating and
+ * allocation-free forms), process-wide: 1 (default) = one launch on small
+ * shards as sp_region_bwd describes, 2 = always the row launch followed by
+ * the column-reduction launch.  Results are bitwise identical; the setting
+ * exists for tests and measurements.  Returns SPR_ERR_INVALID_ARG for other
+ * values.
+ */
+int sp_region_set_bwd_launches(int32_t launches);
 
 /*
  * Calibration kernel: copies nbytes (a multiple of 16) from src to dst with

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libsp_region.so")
 SPR_OK, SPR_ERR_INVALID_ARG, SPR_ERR_UNSUPPORTED, SPR_ERR_ALIGNMENT, SPR_ERR_HIP, SPR_ERR_SCRATCH = range(6)
 SPR_F32, SPR_BF16 = 0, 1
 SPR_LAYERNORM, SPR_RMSNORM = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 NOALLOC_SCRATCH_BYTES = 32 << 20     # SPR_NOALLOC_SCRATCH_BYTES
 
 # Every symbol include/sp_region.h declares, with its ctypes signature.
@@ -54,6 +54,7 @@ SIGNATURES = {
                                                 _F32, _I32, _U64, _VP, _I32,
                                                 _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "sp_region_hbm_copy": (ctypes.c_int, [_VP, _VP, _SZ, _VP]),
+    "sp_region_set_bwd_launches": (ctypes.c_int, [_I32]),
     "sp_region_cv_within": (ctypes.c_int, [_VP, _I32, _I32, _VP]),
     "sp_region_bucket_by_tokens": (ctypes.c_int, [_VP, _I32, _I32, _I64, _VP, _VP, _VP]),
     "sp_region_sp_gate": (ctypes.c_int, [_VP, _I32, ctypes.c_double, _I32, ctypes.c_double, _VP]),
@@ -412,6 +413,11 @@ def bwd_dropout(dy, z, mean, rstd, gamma, *, b: int, s: int, t: int, rank: int, 
                           _ptr(dgamma), _ptr(dbeta), _ptr(dbias), _ptr(workspace), workspace.numel(), stream)
     _check(fn, st)
     return BwdDropoutOut(dx, dpartial, dgamma, dbeta, dbias)
+
+
+def set_bwd_launches(n: int) -> None:
+    """1: small-shard backward in one launch (default); 2: always the partials' two launches."""
+    _check("sp_region_set_bwd_launches", load_library().sp_region_set_bwd_launches(n))
 
 
 def hbm_copy(src, dst) -> None:

@@ -197,14 +197,12 @@ int64_t sp_region_partials_stride(int64_t n_local_tokens, int64_t h, int32_t dty
 
 size_t sp_region_bwd_workspace_bytes(int64_t n_local_tokens, int64_t h) {
   if (n_local_tokens <= 0 || h <= 0) return 0;
-  return static_cast<size_t>(spr::bwd_blocks(n_local_tokens, h)) * static_cast<size_t>(spr::ws_block_stride(h, 2)) *
-         sizeof(float);
+  return static_cast<size_t>(spr::ws_total_bytes(spr::bwd_blocks(n_local_tokens, h), h, 2));
 }
 
 size_t sp_region_bwd_dropout_workspace_bytes(int64_t n_local_tokens, int64_t h) {
   if (n_local_tokens <= 0 || h <= 0) return 0;
-  return static_cast<size_t>(spr::bwd_blocks(n_local_tokens, h)) * static_cast<size_t>(spr::ws_block_stride(h, 3)) *
-         sizeof(float);
+  return static_cast<size_t>(spr::ws_total_bytes(spr::bwd_blocks(n_local_tokens, h), h, 3));
 }
 
 }  // extern "C"
@@ -345,6 +343,12 @@ int sp_region_bwd_accumulate(int64_t b, int64_t s, int64_t h, int32_t t,
   if (with_dropout) set_dropout(&p, t, p_drop, rank, seed, cu_seqlens, nseq, dpartial, dbias);
   p.accumulate = 1;
   return hip_status(spr::launch_bwd(p, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int sp_region_set_bwd_launches(int32_t launches) {
+  if (launches != 1 && launches != 2) return SPR_ERR_INVALID_ARG;
+  spr::set_bwd_launches(launches);
+  return SPR_OK;
 }
 
 int sp_region_hbm_copy(const void* src, void* dst, size_t nbytes, void* stream) {

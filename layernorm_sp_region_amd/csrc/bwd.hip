@@ -10,19 +10,27 @@
 // the same section): dpartial = dx * keep * scale with the forward's own
 // mask, the gradient of every slab, and dbias_j = sum_i dpartial_ij.
 //
-// Stage 1 (sp_region_bwd_rows_kernel): G blocks, block b owns rows b, b + G,
-// b + 2G, ... (interleaved, so the rows the G blocks read at one moment form
-// one contiguous band of memory; contiguous runs of T/G rows per block put
-// the concurrent reads T/G rows apart, a power-of-two stride at the usual
-// shapes, which measured 2-9% slower).  Each thread owns a fixed set of columns, keeps
-// their gamma and their dgamma/dbeta (/dbias) running sums in registers
-// across rows, and the block writes one float32 partial per gradient to the
-// workspace.  Rows stream through a ring of RING packed row buffers (RING
-// rows in flight per block); each row's two sums take one block reduction.
+// Rows.  G blocks; block b owns rows b, b + G, b + 2G, ... (interleaved, so
+// the rows the G blocks read at one moment form one contiguous band of
+// memory).  Each thread owns a fixed set of columns: it keeps their gamma and
+// their dgamma/dbeta (/dbias) running sums in registers across rows.  A
+// block of at most R rows loads them all at once and takes ONE barrier for
+// their row sums; longer blocks stream rows through a ring.  (Measured at the
+// 70B shard: all 8 rows of a block in flight with one barrier, 20 us for the
+// row work; one row per barrier with 4 rows in flight, 24 us.)
 //
-// Stage 2 (sp_region_bwd_cols_kernel): each gradient = the G partials summed
-// in ascending block order, split over 32 groups whose sums are combined in
-// group order -- a fixed tree, so results are bitwise reproducible.
+// Column sums, in one fixed tree whatever the path, so results are bitwise
+// reproducible: row block b's rows in row order; 32 groups of blocks (g,
+// g + 32, ...), each summed in ascending block order; then the 32 group sums
+// in group order.  Two ways to evaluate it:
+//   * partials (any shard): every row block writes its column sums to the
+//     workspace and a second kernel sums them down the tree;
+//   * direct (small shards without the dropout, one launch): column blocks
+//     beside the row blocks evaluate the same tree from dy, z, mean and rstd
+//     themselves, so no partial is written and nothing waits on another
+//     block.
+
+#include <atomic>
 
 #include "spr_device.h"
 #include "spr_internal.h"
@@ -30,172 +38,233 @@
 namespace spr {
 namespace {
 
-#ifndef SPR_BWD_NT_STORE
-#define SPR_BWD_NT_STORE 1        // nontemporal stores for dx (measured: the next kernel no longer
-                                  // pays for writing back dirty dx lines)
-#endif
-
+// One row of a [T][h] tensor as a buffer resource of `bytes` bytes (0 makes
+// every load of it out of range: zeros, no memory access); loads are
+// nontemporal (streamed once).
+constexpr int kCpolNontemporal = 2;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const char* row, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(row), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 ld16_row(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kCpolNontemporal));
+}
+// Nontemporal store (measured: the next kernel no longer pays for writing
+// back dirty dx lines).
 __device__ __forceinline__ void st16_dx(void* p, u32x4 v) {
-  if constexpr (SPR_BWD_NT_STORE) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-  else st16(p, v);
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
-#ifndef SPR_WS_NT
-#define SPR_WS_NT 0
+#ifndef SPR_BWD_MAX_THREADS
+#define SPR_BWD_MAX_THREADS 512   // block size cap of the row stage
 #endif
-__device__ __forceinline__ void st16_ws(void* p, u32x4 v) {
-  if constexpr (SPR_WS_NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-  else st16(p, v);
-}
 
-// Packed loads of one row: VPT vectors of dy, z (and dres) per thread.
-// The row's statistics travel with its data: every lane loads the same
-// mean/rstd (one broadcast request per wave), so waiting for a ring slot
-// never waits on loads issued after it (vmcnt completes in issue order).
-template <int VPT, bool DRES>
-struct RowBuf {
-  u32x4 dy[VPT], z[VPT], dr[DRES ? VPT : 1];
-  float mu, rs;
-  uint32_t g_lo, g_hi;   // global token index of the row (dropout backward)
+// Packed loads of N rows: VPT vectors of dy, z (and dres) per thread per
+// row.  A row's statistics travel with its data: every lane loads the same
+// mean/rstd (one broadcast request per wave), so waiting for a row never
+// waits on loads issued after it (vmcnt completes in issue order).
+template <int VPT, int N, bool DRES>
+struct Rows {
+  u32x4 dy[N][VPT], z[N][VPT], dr[DRES ? N : 1][DRES ? VPT : 1];
+  float mu[N], rs[N];
+  uint32_t g_lo[N], g_hi[N];   // global token index of each row (dropout backward)
 };
 
-// Stage 1 for block blockIdx.x: dx of its rows (and, with DROP, dpartial =
-// dx*keep*scale), and its partials of dgamma, dbeta (and dbias) in the
-// workspace: slot j of block b at ws + b*ws_bstride + j*ws_sstride.
-template <class E, int VPT, int RING, bool DRES, bool DROP>
-__device__ __forceinline__ void rows_stage(const BwdParams& p) {
+// Column state of one block: the running sums of its columns (and their
+// gamma, unpacked, when it fits the registers).
+template <int VPT, int V, bool DROP>
+struct ColSums {
+  static constexpr bool kGammaLds = VPT >= 4;   // wide rows keep gamma packed in LDS
+  int vv[VPT];       // vector index of slot k (clamped to the row)
+  bool valid[VPT];   // slot k holds a vector of the row
+  float gam[kGammaLds ? 1 : VPT][V], dg[VPT][V], db[VPT][V];
+  float dbs[DROP ? VPT : 1][V];
+};
+
+// Rows of block b: local row li is global row b + li*G (G <= T, so every
+// block has at least one row), r1 of them.
+__device__ __forceinline__ int block_rows(const BwdParams& p) {
+  return static_cast<int>((p.T - blockIdx.x + p.G - 1) / p.G);
+}
+
+template <class E, int VPT, bool DROP>
+__device__ __forceinline__ void init_cols(const BwdParams& p, ColSums<VPT, E::kVec, DROP>& cs,
+                                          u32x4 (*gl)[SPR_BWD_MAX_THREADS]) {
   constexpr int V = E::kVec;
-  constexpr int EB = 16 / V;
-  __shared__ float red[2][2 * 16];
-
   const int tid = threadIdx.x;
-  const int bs = blockDim.x;
-  const int lane = tid & (kWave - 1), wave = tid / kWave, nwaves = bs / kWave;
-  const int h = p.h;
-  const int nvec = h / V;
-  // Local row li of this block is global row blockIdx.x + li*G (G <= T, so
-  // every block has at least one row).
-  const int r0 = 0;
-  const int r1 = static_cast<int>((p.T - blockIdx.x + p.G - 1) / p.G);
-  const int bx = blockIdx.x, G = p.G;
-  auto grow = [=](int li) { return bx + li * G; };
-  const bool ln = p.norm == 0;
-  const float inv_h = 1.0f / static_cast<float>(h);
-
-  int vv[VPT];
-  bool valid[VPT];
-  float gam[VPT][V], dg[VPT][V], db[VPT][V];
-  float dbs[DROP ? VPT : 1][V];   // dbias running sums
+  const int nvec = p.h / V;
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    const int v = tid + k * bs;
-    valid[k] = v < nvec;
-    vv[k] = valid[k] ? v : nvec - 1;   // clamped: loads stay in bounds
-    unpack(E{}, ld16(static_cast<const char*>(p.gamma) + vv[k] * 16), gam[k]);
+    const int v = tid + k * static_cast<int>(blockDim.x);
+    cs.valid[k] = v < nvec;
+    cs.vv[k] = cs.valid[k] ? v : nvec - 1;   // clamped: loads stay in bounds
+    const u32x4 gv = ld16(static_cast<const char*>(p.gamma) + cs.vv[k] * 16);
+    if constexpr (ColSums<VPT, V, DROP>::kGammaLds) gl[k][tid] = gv;
+    else unpack(E{}, gv, cs.gam[k]);
 #pragma unroll
-    for (int e = 0; e < V; ++e) dg[k][e] = db[k][e] = 0.0f;
+    for (int e = 0; e < V; ++e) cs.dg[k][e] = cs.db[k][e] = 0.0f;
     if constexpr (DROP) {
 #pragma unroll
-      for (int e = 0; e < V; ++e) dbs[k][e] = 0.0f;
+      for (int e = 0; e < V; ++e) cs.dbs[k][e] = 0.0f;
     }
   }
+}
 
-  // Rows stream through a ring of RING row buffers: row r + RING is issued
-  // as soon as row r has been consumed, so RING rows stay in flight.  The
-  // loads are unconditional (no branch for the waitcnt pass to merge over,
-  // which would force it to drain every outstanding load): past the block's
-  // last row they read gamma instead, an in-bounds, L2-resident stand-in whose
-  // values are never used.
-  const char* stand_in = static_cast<const char*>(p.gamma);
-  auto issue = [&](RowBuf<VPT, DRES>& b, int row) {
-    const bool live = row < r1;   // block-uniform
-    const int64_t off = static_cast<int64_t>(grow(row)) * h * EB;
-    const char* dyp = live ? static_cast<const char*>(p.dy) + off : stand_in;
-    const char* zp = live ? static_cast<const char*>(p.z) + off : stand_in;
-    const char* drp = DRES && live ? static_cast<const char*>(p.dres) + off : stand_in;
+template <class E, int VPT, bool DROP>
+__device__ __forceinline__ void gamma_of(const ColSums<VPT, E::kVec, DROP>& cs, u32x4 (*gl)[SPR_BWD_MAX_THREADS],
+                                         int k, float (&g)[E::kVec]) {
+  if constexpr (ColSums<VPT, E::kVec, DROP>::kGammaLds) {
+    unpack(E{}, gl[k][threadIdx.x], g);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E::kVec; ++e) g[e] = cs.gam[k][e];
+  }
+}
+
+// Issue the loads of local rows li0 .. li0+N-1.  Every load is unconditional
+// (no branch for the waitcnt pass to merge over, which would make it drain
+// every outstanding load): each row is read through a buffer resource based
+// at the row, whose size is the row's for a row of the block and 0 past the
+// block's last row -- those loads are out of range, so the hardware returns
+// zeros without touching memory.
+template <class E, int VPT, int N, bool DRES, bool DROP>
+__device__ __forceinline__ void issue_rows(const BwdParams& p, const ColSums<VPT, E::kVec, DROP>& cs,
+                                           Rows<VPT, N, DRES>& b, int li0, int r1) {
+  constexpr int EB = 16 / E::kVec;
+  const int h = p.h;
+  const int bx = blockIdx.x, G = p.G;
+  const bool ln = p.norm == 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const int li = li0 + j;
+    const bool live = li < r1;   // block-uniform
+    const int lc = live ? li : r1 - 1;
+    const int64_t off = static_cast<int64_t>(bx + static_cast<int64_t>(lc) * G) * h * EB;
+    const int bytes = live ? h * EB : 0;
+    const auto rdy = row_rsrc(static_cast<const char*>(p.dy) + off, bytes);
+    const auto rz = row_rsrc(static_cast<const char*>(p.z) + off, bytes);
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      b.dy[k] = ld16_stream(dyp + vv[k] * 16);
-      b.z[k] = ld16_stream(zp + vv[k] * 16);
-      if constexpr (DRES) b.dr[k] = ld16_stream(drp + vv[k] * 16);
+      b.dy[j][k] = ld16_row(rdy, cs.vv[k] * 16);
+      b.z[j][k] = ld16_row(rz, cs.vv[k] * 16);
     }
-    const int srow = grow(live ? row : r1 - 1);
-    b.mu = ln ? p.mean[srow] : 0.0f;
-    b.rs = p.rstd[srow];
+    if constexpr (DRES) {
+      const auto rdr = row_rsrc(static_cast<const char*>(p.dres) + off, bytes);
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) b.dr[j][k] = ld16_row(rdr, cs.vv[k] * 16);
+    }
+    const int64_t srow = bx + static_cast<int64_t>(lc) * G;
+    b.mu[j] = ln ? p.mean[srow] : 0.0f;
+    b.rs[j] = p.rstd[srow];
     if constexpr (DROP) {
-      // Scalar loads only (ragged offsets): no wait on the ring's vector loads.
+      // Scalar loads only (ragged offsets): no wait on the rows' vector loads.
       const uint64_t g = p.drop ? global_token_of(srow, p.T, p.t, p.rank, p.cu, p.nseq) : 0;
-      b.g_lo = static_cast<uint32_t>(g);
-      b.g_hi = static_cast<uint32_t>(g >> 32);
+      b.g_lo[j] = static_cast<uint32_t>(g);
+      b.g_hi[j] = static_cast<uint32_t>(g >> 32);
     }
-  };
+  }
+}
 
-  int parity = 0;
-  auto process = [&](const RowBuf<VPT, DRES>& b, int row) {
-    if (row >= r1) return;   // block-uniform: every thread skips the barrier alike
-    const float mu = b.mu;
-    const float rs = b.rs;
-    // xhat, g and dy of this row stay in registers between the two phases.
-    float xh[VPT][V], gg[VPT][V], dyv[VPT][V];
-    float part[2] = {0.0f, 0.0f};
+// Rows li0 .. li0+N-1 (those below r1): their N pairs of row sums (g,
+// g*xhat) in one block reduction, then dx (and dpartial) stored and, with
+// COLS, the column sums advanced, in row order.
+// slot: LDS of 2*N*16 floats, alternated between consecutive calls by the
+// caller (one barrier per call).
+template <class E, int VPT, int N, bool DRES, bool DROP, bool COLS = true>
+__device__ __forceinline__ void finish_rows(const BwdParams& p, ColSums<VPT, E::kVec, DROP>& cs,
+                                            u32x4 (*gl)[SPR_BWD_MAX_THREADS], Rows<VPT, N, DRES>& b, int li0,
+                                            int r1, float (*slot)[N][16]) {
+  constexpr int V = E::kVec;
+  constexpr int EB = 16 / V;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave, nwaves = blockDim.x / kWave;
+  const int h = p.h;
+  const bool ln = p.norm == 0;
+  const float inv_h = 1.0f / static_cast<float>(h);
+  float part[2 * N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    part[2 * j] = part[2 * j + 1] = 0.0f;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      float zv[V];
-      unpack(E{}, b.z[k], zv);
-      unpack(E{}, b.dy[k], dyv[k]);
+      float zv[V], dyv[V], gm[V];
+      unpack(E{}, b.z[j][k], zv);
+      unpack(E{}, b.dy[j][k], dyv);
+      gamma_of<E, VPT, DROP>(cs, gl, k, gm);
       float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        xh[k][e] = (zv[e] - mu) * rs;
-        gg[k][e] = dyv[k][e] * gam[k][e];
-        p0 += gg[k][e];
-        p1 = __builtin_fmaf(gg[k][e], xh[k][e], p1);
+        const float xh = (zv[e] - b.mu[j]) * b.rs[j];
+        const float gg = dyv[e] * gm[e];
+        p0 += gg;
+        p1 = __builtin_fmaf(gg, xh, p1);
       }
-      part[0] += valid[k] ? p0 : 0.0f;
-      part[1] += valid[k] ? p1 : 0.0f;
+      part[2 * j] += cs.valid[k] ? p0 : 0.0f;
+      part[2 * j + 1] += cs.valid[k] ? p1 : 0.0f;
     }
-    // One barrier per row; the two LDS slots alternate, so a slot is only
-    // rewritten after every wave has passed the barrier of the row between.
-    float* slot = red[parity];
-    parity ^= 1;
-    wave_sum<2>(part);
-    if (lane == 0) {
-      slot[wave] = part[0];
-      slot[16 + wave] = part[1];
+  }
+  wave_sum<2 * N>(part);
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      slot[0][j][wave] = part[2 * j];
+      slot[1][j][wave] = part[2 * j + 1];
     }
-    __syncthreads();
-    float s1 = slot[0], s2 = slot[16];
+  }
+  __syncthreads();
+  // Several rows: the packed rows are unpacked again below rather than kept
+  // unpacked across the barrier (N rows of unpacked floats would not fit the
+  // registers).  One row (the ring): the compiler may keep them unpacked.
+  if constexpr (N > 1) {
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        asm volatile("" : "+v"(b.dy[j][k]));
+        asm volatile("" : "+v"(b.z[j][k]));
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const int li = li0 + j;
+    if (li >= r1) continue;   // block-uniform
+    float s1 = slot[0][j][0], s2 = slot[1][j][0];
     for (int w = 1; w < nwaves; ++w) {   // wave order: the same total in every thread
-      s1 += slot[w];
-      s2 += slot[16 + w];
+      s1 += slot[0][j][w];
+      s2 += slot[1][j][w];
     }
     const float c1 = ln ? s1 * inv_h : 0.0f;
     const float c2 = s2 * inv_h;
-    const int64_t off = static_cast<int64_t>(grow(row)) * h * EB;
+    const int64_t off = static_cast<int64_t>(blockIdx.x + static_cast<int64_t>(li) * p.G) * h * EB;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      if (!valid[k]) continue;
-      float dx[V];
+      if (!cs.valid[k]) continue;
+      float zv[V], dyv[V], gm[V], dx[V];
+      unpack(E{}, b.z[j][k], zv);
+      unpack(E{}, b.dy[j][k], dyv);
+      gamma_of<E, VPT, DROP>(cs, gl, k, gm);
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        dx[e] = rs * __builtin_fmaf(-xh[k][e], c2, gg[k][e] - c1);
-        dg[k][e] = __builtin_fmaf(dyv[k][e], xh[k][e], dg[k][e]);
-        db[k][e] += dyv[k][e];
+        const float xh = (zv[e] - b.mu[j]) * b.rs[j];
+        const float gg = dyv[e] * gm[e];
+        dx[e] = b.rs[j] * __builtin_fmaf(-xh, c2, gg - c1);
+        if constexpr (COLS) {
+          cs.dg[k][e] = __builtin_fmaf(dyv[e], xh, cs.dg[k][e]);
+          cs.db[k][e] += dyv[e];
+        }
       }
       if constexpr (DRES) {
         float f[V];
-        unpack(E{}, b.dr[k], f);
+        unpack(E{}, b.dr[j][k], f);
 #pragma unroll
         for (int e = 0; e < V; ++e) dx[e] += f[e];
       }
-      st16_dx(static_cast<char*>(p.dx) + off + vv[k] * 16, pack(E{}, dx));
+      st16_dx(static_cast<char*>(p.dx) + off + cs.vv[k] * 16, pack(E{}, dx));
       if constexpr (DROP) {
         // Through the dropout: kept channels times the forward's scale, the
         // forward's own mask (same seed, same global token).
         float dp[V];
         if (p.drop) {
           bool keep[V];
-          dropout_keep<V>(static_cast<uint32_t>(vv[k]), b.g_lo, b.g_hi, p.key0, p.key1, p.thr, keep);
+          dropout_keep<V>(static_cast<uint32_t>(cs.vv[k]), b.g_lo[j], b.g_hi[j], p.key0, p.key1, p.thr, keep);
 #pragma unroll
           for (int e = 0; e < V; ++e) dp[e] = keep[e] ? dx[e] * p.scale : 0.0f;
         } else {
@@ -203,167 +272,293 @@ __device__ __forceinline__ void rows_stage(const BwdParams& p) {
           for (int e = 0; e < V; ++e) dp[e] = dx[e];
         }
 #pragma unroll
-        for (int e = 0; e < V; ++e) dbs[k][e] += dp[e];
-        st16_dx(static_cast<char*>(p.dpartial) + off + vv[k] * 16, pack(E{}, dp));
+        for (int e = 0; e < V; ++e) cs.dbs[k][e] += dp[e];
+        st16_dx(static_cast<char*>(p.dpartial) + off + cs.vv[k] * 16, pack(E{}, dp));
       }
     }
-  };
-
-  RowBuf<VPT, DRES> ring[RING];
-#pragma unroll
-  for (int j = 0; j < RING; ++j) issue(ring[j], r0 + j);
-  for (int r = r0; r < r1; r += RING) {
-#pragma unroll
-    for (int j = 0; j < RING; ++j) {
-      process(ring[j], r + j);
-      issue(ring[j], r + j + RING);
-    }
   }
+}
 
-  // Partial slots: dgamma first, then dbeta and dbias where requested.
-  float* ws = p.ws + static_cast<int64_t>(blockIdx.x) * p.ws_bstride;
-  auto put = [&](float* dst, const float (&a)[V], int k) {
+// The rows of block blockIdx.x, R at a time (SHORT: the block has at most R
+// rows, all loaded at once, one barrier -- straight-line code), or one at a
+// time through a ring of R rows in flight (long shards).  dx (and dpartial)
+// stored; then store_cols() with the block's column sums complete.
+template <class E, int VPT, int R, bool SHORT, bool DRES, bool DROP, class Hook, bool COLS = true>
+__device__ __forceinline__ void rows_phase(const BwdParams& p, ColSums<VPT, E::kVec, DROP>& cs,
+                                           const Hook& store_cols) {
+  __shared__ float red[2][2][SHORT ? R : 1][16];   // [parity][sum][row][wave]
+  __shared__ u32x4 gam_lds[ColSums<VPT, E::kVec, DROP>::kGammaLds ? VPT : 1][SPR_BWD_MAX_THREADS];
+  init_cols<E, VPT, DROP>(p, cs, gam_lds);
+  const int r1 = block_rows(p);
+  if constexpr (SHORT) {
+    Rows<VPT, R, DRES> b;
+    issue_rows<E, VPT, R, DRES, DROP>(p, cs, b, 0, r1);
+    finish_rows<E, VPT, R, DRES, DROP, COLS>(p, cs, gam_lds, b, 0, r1, red[0]);
+    if constexpr (COLS) store_cols();
+  } else {
+    // A ring of R single rows: row li + R is issued as soon as row li has
+    // been consumed; one barrier per row, the two LDS slots alternating.
+    Rows<VPT, 1, DRES> ring[R];
 #pragma unroll
-    for (int e0 = 0; e0 < V; e0 += 4)
-      st16_ws(dst + vv[k] * V + e0, u32x4{__float_as_uint(a[e0]), __float_as_uint(a[e0 + 1]),
-                                          __float_as_uint(a[e0 + 2]), __float_as_uint(a[e0 + 3])});
+    for (int j = 0; j < R; ++j) issue_rows<E, VPT, 1, DRES, DROP>(p, cs, ring[j], j, r1);
+    int parity = 0;
+    for (int li = 0; li < r1; li += R) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        if (li + j < r1) {   // block-uniform
+          finish_rows<E, VPT, 1, DRES, DROP, COLS>(p, cs, gam_lds, ring[j], li + j, r1, red[parity]);
+          parity ^= 1;
+        }
+        issue_rows<E, VPT, 1, DRES, DROP>(p, cs, ring[j], li + j + R, r1);
+      }
+    }
+    if constexpr (COLS) store_cols();
+  }
+}
+
+// Block blockIdx.x's partial slots (dgamma first, then dbeta and dbias where
+// requested) at ws + b*bstride + slot*sstride.
+template <int VPT, int V, bool DROP>
+__device__ __forceinline__ void store_partials(const BwdParams& p, const ColSums<VPT, V, DROP>& cs) {
+  float* base = p.ws + static_cast<int64_t>(blockIdx.x) * p.ws_bstride;
+  auto put = [&](int slot, const float (&a)[V], int k) {
+    float* dst = base + slot * p.ws_sstride + cs.vv[k] * V;
+#pragma unroll
+    for (int e0 = 0; e0 < V; e0 += 4) {
+      const u32x4 v{__float_as_uint(a[e0]), __float_as_uint(a[e0 + 1]), __float_as_uint(a[e0 + 2]),
+                    __float_as_uint(a[e0 + 3])};
+      st16(dst + e0, v);
+    }
   };
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    if (!valid[k]) continue;
-    put(ws, dg[k], k);
-    if (p.slot_dbeta > 0) put(ws + p.slot_dbeta * p.ws_sstride, db[k], k);
+    if (!cs.valid[k]) continue;
+    put(0, cs.dg[k], k);
+    if (p.slot_dbeta > 0) put(p.slot_dbeta, cs.db[k], k);
     if constexpr (DROP) {
-      if (p.slot_dbias > 0) put(ws + p.slot_dbias * p.ws_sstride, dbs[k], k);
+      if (p.slot_dbias > 0) put(p.slot_dbias, cs.dbs[k], k);
     }
   }
 }
 
-template <class E, int VPT, int RING, bool DRES, bool DROP, int MAXBS>
-__global__ __launch_bounds__(MAXBS) void sp_region_bwd_rows_kernel(const BwdParams p) {
-  rows_stage<E, VPT, RING, DRES, DROP>(p);
-}
-
-// Stage 2: the G partials of each column are summed in a fixed tree: 32
-// groups of consecutive partials, each summed in ascending block order, then
-// the 32 group sums in group order.  The tree depends only on G.
-#ifndef SPR_BWD_GROUPS
-#define SPR_BWD_GROUPS 32   // 16 and 64 measured slower (latency-bound loads / half-line segments)
-#endif
-constexpr int kGroups = SPR_BWD_GROUPS;
+// The fixed tree's shape: 32 groups, group g holding the partials of blocks
+// g, g + 32, g + 64, ... (blocks are dealt to the 8 XCDs round-robin, so a
+// group's blocks share an XCD).  The tree depends only on G.
+constexpr int kGroups = 32;
 static_assert(kBwdMaxBlocks % kGroups == 0, "groups must split the partials evenly");
+constexpr int kPerGroup = kBwdMaxBlocks / kGroups;   // partials per group, at most
 
-// Column quads [q0, q1) of the NP partial slots (block b's slot j at
-// ws + b*bstride + j*sstride) into out[j], cw = blockDim.x / kGroups quads at a
-// time (cw <= CQMAX); thread (group, quad) = (threadIdx.x / cw,
-// threadIdx.x % cw).  Every thread of the block calls this (it has barriers).
-template <int CQMAX, int NP>
-__device__ __forceinline__ void reduce_cols(const float* __restrict__ ws, int G, int64_t bstride, int64_t sstride,
-                                            int q0, int q1, bool accumulate,
-                                            float* const (&out)[NP]) {
-  __shared__ float4 part[NP][kGroups][CQMAX];
-  const int cw = static_cast<int>(blockDim.x) / kGroups;
-  const int cq = threadIdx.x % cw;
-  const int grp = threadIdx.x / cw;   // < kGroups since blockDim.x = kGroups * cw
-  // At most kBwdMaxBlocks / kGroups partials per group: all loads in flight
-  // together, then summed in ascending block order.
-  constexpr int kPer = kBwdMaxBlocks / kGroups;
-  const int g0 = grp * G / kGroups, g1 = (grp + 1) * G / kGroups;
-  for (int qb = q0; qb < q1; qb += cw) {   // block-uniform
-    const int c4 = qb + cq;
-    float4 sum[NP];
-#pragma unroll
-    for (int j = 0; j < NP; ++j) sum[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (G > 0) {   // block-uniform; G == 0: no partials exist (the sums stay 0)
-      // Every load is unconditional, from a clamped in-bounds address (a
-      // load under a branch would make the waitcnt pass serialise them);
-      // the bounds are applied by the selects below.
-      const int cc = c4 < q1 ? c4 : q1 - 1;
-      float4 a[NP][kPer];
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int gi = g0 + i < G ? g0 + i : G - 1;
-#pragma unroll
-        for (int j = 0; j < NP; ++j)
-          a[j][i] = reinterpret_cast<const float4*>(ws + gi * bstride + j * sstride)[cc];
-      }
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const bool in = g0 + i < g1;
-#pragma unroll
-        for (int j = 0; j < NP; ++j) {
-          sum[j].x = in ? sum[j].x + a[j][i].x : sum[j].x;
-          sum[j].y = in ? sum[j].y + a[j][i].y : sum[j].y;
-          sum[j].z = in ? sum[j].z + a[j][i].z : sum[j].z;
-          sum[j].w = in ? sum[j].w + a[j][i].w : sum[j].w;
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NP; ++j) part[j][grp][cq] = sum[j];
-    __syncthreads();
-    if (grp == 0 && c4 < q1) {
-#pragma unroll
-      for (int j = 0; j < NP; ++j) {
-        float4 tot = part[j][0][cq];
-        for (int i = 1; i < kGroups; ++i) {
-          const float4 x = part[j][i][cq];
-          tot.x += x.x; tot.y += x.y; tot.z += x.z; tot.w += x.w;
-        }
-        if (accumulate) {   // main gradient: old + this call's sum, one rounding
-          const float4 m = reinterpret_cast<const float4*>(out[j])[c4];
-          tot.x = m.x + tot.x; tot.y = m.y + tot.y; tot.z = m.z + tot.z; tot.w = m.w + tot.w;
-        }
-        reinterpret_cast<float4*>(out[j])[c4] = tot;
-      }
-    }
-    __syncthreads();   // part is rewritten by the next chunk
-  }
-}
-
-#ifndef SPR_COLS_QPB
-#define SPR_COLS_QPB 8    // column quads per block of stage 2: 128-byte segments of each partial
-#endif
-constexpr int kColQuads = SPR_COLS_QPB;
-
-// Outputs of stage 2, slot order (dgamma, then dbeta / dbias where requested).
+// Outputs of the column sums, slot order (dgamma, then dbeta / dbias where requested).
 struct ColOut {
   float* p[3];
+  int32_t np;           // slots in use (1..3)
   int32_t accumulate;   // nonzero: out = old + sum
 };
+
+// Row block kernel of the partials path: dx (and dpartial), then the block's
+// column sums to the workspace.
+template <class E, int VPT, int R, bool SHORT, bool DRES, bool DROP, int MAXBS>
+__global__ __launch_bounds__(MAXBS) void sp_region_bwd_rows_kernel(const BwdParams p) {
+  ColSums<VPT, E::kVec, DROP> cs;
+  rows_phase<E, VPT, R, SHORT, DRES, DROP>(p, cs, [&] { store_partials<VPT, E::kVec, DROP>(p, cs); });
+}
+
+// Second kernel of the partials path: column quads [q0, q0 + kColQuads) of
+// the NP partial slots into o.p[j], thread (group, quad) = (threadIdx.x /
+// kColQuads, threadIdx.x % kColQuads).  NP >= o.np is the compile-time slot
+// count: slots o.np..NP-1 re-read slot 0 (the same addresses, no extra
+// traffic) and are never stored.
+#ifndef SPR_COLS_QPB
+#define SPR_COLS_QPB 8    // column quads per block: 128-byte segments
+#endif
+constexpr int kColQuads = SPR_COLS_QPB;
 
 template <int NP>
 __global__ __launch_bounds__(kColQuads * kGroups) void sp_region_bwd_cols_kernel(const float* __restrict__ ws, int G,
                                                                                  int h, int64_t bstride,
                                                                                  int64_t sstride, ColOut o) {
+  __shared__ float4 part[NP][kGroups][kColQuads];
   const int nq = h / 4;
-  const int q0 = blockIdx.x * kColQuads;
-  float* out[NP];
+  const int cq = threadIdx.x % kColQuads;
+  const int grp = threadIdx.x / kColQuads;
+  const int c4 = blockIdx.x * kColQuads + cq;
+  int64_t soff[NP];
 #pragma unroll
-  for (int j = 0; j < NP; ++j) out[j] = o.p[j];
-  reduce_cols<kColQuads, NP>(ws, G, bstride, sstride, q0, q0 + kColQuads < nq ? q0 + kColQuads : nq,
-                             o.accumulate != 0, out);
+  for (int j = 0; j < NP; ++j) soff[j] = (j < o.np ? j : 0) * sstride;
+  // Every load is unconditional, from a clamped in-bounds address (a load
+  // under a branch would make the waitcnt pass serialise them); the bounds
+  // are applied by the selects below.  G == 0: no partials (sums stay 0).
+  const int cc = c4 < nq ? c4 : nq - 1;
+  float4 a[NP][kPerGroup];
+#pragma unroll
+  for (int i = 0; i < kPerGroup; ++i) {
+    const int b = grp + i * kGroups;
+    const int gi = b < G ? b : (G > 0 ? G - 1 : 0);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) a[j][i] = reinterpret_cast<const float4*>(ws + gi * bstride + soff[j] + 4 * cc)[0];
+  }
+  float4 sum[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) sum[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < kPerGroup; ++i) {
+    const bool in = grp + i * kGroups < G;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      sum[j].x = in ? sum[j].x + a[j][i].x : sum[j].x;
+      sum[j].y = in ? sum[j].y + a[j][i].y : sum[j].y;
+      sum[j].z = in ? sum[j].z + a[j][i].z : sum[j].z;
+      sum[j].w = in ? sum[j].w + a[j][i].w : sum[j].w;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NP; ++j) part[j][grp][cq] = sum[j];
+  __syncthreads();
+  if (grp == 0 && c4 < nq) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      if (j >= o.np) continue;
+      float4 tot = part[j][0][cq];
+      for (int i = 1; i < kGroups; ++i) {
+        const float4 x = part[j][i][cq];
+        tot.x += x.x; tot.y += x.y; tot.z += x.z; tot.w += x.w;
+      }
+      if (o.accumulate) {   // main gradient: old + this call's sum, one rounding
+        const float4 m = reinterpret_cast<const float4*>(o.p[j])[c4];
+        tot.x = m.x + tot.x; tot.y = m.y + tot.y; tot.z = m.z + tot.z; tot.w = m.w + tot.w;
+      }
+      reinterpret_cast<float4*>(o.p[j])[c4] = tot;
+    }
+  }
 }
 
-#ifndef SPR_BWD_MAX_THREADS
-#define SPR_BWD_MAX_THREADS 512   // block size cap of the row stage
+// The direct path (small shards, no dropout): the same launch holds the G
+// row blocks, which store dx and keep no column sums, and column blocks,
+// each of which sums dgamma/dbeta for kDirectLanes vectors of columns straight
+// from dy, z, mean and rstd.  No partials leave the block, so there is no
+// workspace, flag or second launch -- and the column blocks reproduce the
+// partials path's tree exactly (row block b's rows in order, from 0; the 32
+// groups of blocks g, g + 32, ... in order, from 0; then the groups in
+// order), so the result is bitwise the same whichever path runs.
+#ifndef SPR_BWD_DIRECT_LANES
+#define SPR_BWD_DIRECT_LANES 4
 #endif
-#ifndef SPR_BWD_RING
-#define SPR_BWD_RING 4            // rows in flight per block
-#endif
+constexpr int kDirectLanes = SPR_BWD_DIRECT_LANES;   // 16-byte vectors per row segment of a column block
+constexpr int kDirectMaxBlocks = 128;   // row blocks the column blocks' LDS holds
 
-// Ring depth per vectors-per-thread, so the packed ring fits the VGPRs the
-// block size leaves (wider rows keep fewer rows in flight).
-template <int VPT, int MAXBS, bool DROP>
-constexpr int ring_for() {
-  return VPT == 1 ? SPR_BWD_RING : (VPT == 2 && MAXBS <= 512 ? SPR_BWD_RING : (VPT == 2 ? 2 : 1));
+template <class E, int R>
+__device__ __forceinline__ void col_block(const BwdParams& p, const ColOut& o, int c) {
+  constexpr int V = E::kVec, EB = 16 / V, L = kDirectLanes, W = L * V;
+  __shared__ float sb[2][kDirectMaxBlocks][W];   // [dgamma|dbeta][row block][column]
+  __shared__ float grp[2][kGroups][W];
+  const int G = p.G, h = p.h, nvec = h / V;
+  const int t = threadIdx.x, nt = static_cast<int>(blockDim.x);
+  const int lc = t % L, rl = t / L, RL = nt / L;
+  const int v = c * L + lc;
+  const int64_t voff = static_cast<int64_t>(v < nvec ? v : nvec - 1) * 16;
+  const bool ln = p.norm == 0;
+  // Row block b's sums, one row block per row lane at a time: its (at most
+  // R) rows loaded together (rows past the block's last re-read that row and
+  // are not summed), then summed in row order.  The rows differ across the
+  // lanes of a wave, so these are plain per-lane loads.
+  for (int b = rl; b < G; b += RL) {
+    const int r1 = static_cast<int>((p.T - b + G - 1) / G);
+    u32x4 dy[R], z[R];
+    float mu[R], rs[R];
+#pragma unroll
+    for (int li = 0; li < R; ++li) {
+      const int64_t row = b + static_cast<int64_t>(li < r1 ? li : r1 - 1) * G;
+      const int64_t off = row * h * EB + voff;
+      dy[li] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const char*>(p.dy) + off));
+      z[li] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const char*>(p.z) + off));
+      mu[li] = ln ? p.mean[row] : 0.0f;
+      rs[li] = p.rstd[row];
+    }
+    float dg[V], db[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) dg[e] = db[e] = 0.0f;
+#pragma unroll
+    for (int li = 0; li < R; ++li) {
+      if (li >= r1) break;
+      float zv[V], dyv[V];
+      unpack(E{}, z[li], zv);
+      unpack(E{}, dy[li], dyv);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float xh = (zv[e] - mu[li]) * rs[li];
+        dg[e] = __builtin_fmaf(dyv[e], xh, dg[e]);
+        db[e] += dyv[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      sb[0][b][lc * V + e] = dg[e];
+      sb[1][b][lc * V + e] = db[e];
+    }
+  }
+  __syncthreads();
+  for (int q = t; q < kGroups * W; q += nt) {
+    const int g = q / W, col = q % W;
+    float s0 = 0.0f, s1 = 0.0f;
+    for (int i = 0; i < kPerGroup; ++i) {
+      const int b = g + i * kGroups;
+      if (b < G) {
+        s0 += sb[0][b][col];
+        s1 += sb[1][b][col];
+      }
+    }
+    grp[0][g][col] = s0;
+    grp[1][g][col] = s1;
+  }
+  __syncthreads();
+  for (int q = t; q < W * o.np; q += nt) {
+    const int j = q / W, col = q % W;
+    const int64_t gc = static_cast<int64_t>(c) * W + col;
+    if (gc >= h) continue;
+    float tot = grp[j][0][col];
+    for (int g = 1; g < kGroups; ++g) tot += grp[j][g][col];
+    if (o.accumulate) tot = o.p[j][gc] + tot;
+    o.p[j][gc] = tot;
+  }
 }
 
-hipError_t launch_cols(const BwdParams& p, hipStream_t stream) {
-  ColOut o{{p.dgamma, nullptr, nullptr}, p.accumulate};
-  int np = 1;
-  if (p.slot_dbeta > 0) o.p[np++] = p.dbeta;
-  if (p.slot_dbias > 0) o.p[np++] = p.dbias;
+// Blocks [0, G): rows (SHORT, at most R each, no column sums); blocks
+// [G, G + ceil(h / (kDirectLanes * V))): columns.  Nothing waits on another
+// block.
+template <class E, int VPT, int R, bool DRES, int MAXBS>
+__global__ __launch_bounds__(MAXBS) void sp_region_bwd_direct_kernel(const BwdParams p, const ColOut o) {
+  if (static_cast<int>(blockIdx.x) >= p.G) {
+    col_block<E, R>(p, o, static_cast<int>(blockIdx.x) - p.G);
+    return;
+  }
+  ColSums<VPT, E::kVec, false> cs;
+  rows_phase<E, VPT, R, true, DRES, false, int, false>(p, cs, 0);
+}
+
+// Rows in flight for VPT vectors per thread: the packed rows take at most
+// 128 VGPRs; 96 with dres, 64 at 4 vectors per thread or for the dropout
+// backward's extra state, 32 for both (beyond those budgets the kernels
+// spill).  A block of at most that many rows runs straight-line code (all
+// its rows loaded at once, one barrier); longer ones stream their rows
+// through a ring of at most 4.
+#ifndef SPR_BWD_MAX_R
+#define SPR_BWD_MAX_R 8
+#endif
+
+template <int VPT, bool DRES, bool DROP>
+constexpr int rows_in_flight() {
+  constexpr int budget = DROP ? (VPT >= 4 ? 32 : 64) : (DRES ? 96 : (VPT >= 4 ? 64 : 128));
+  constexpr int per_row = VPT * (DRES ? 3 : 2) * 4;
+  constexpr int r = budget / per_row;
+  return r < 1 ? 1 : (r > SPR_BWD_MAX_R ? SPR_BWD_MAX_R : r);
+}
+template <int VPT, bool DRES, bool DROP>
+constexpr int ring_rows() {
+  constexpr int r = rows_in_flight<VPT, DRES, DROP>();
+  return r > 4 ? 4 : r;
+}
+
+hipError_t launch_cols(const BwdParams& p, const ColOut& o, int np, hipStream_t stream) {
   const int nq = p.h / 4;
   const dim3 grid((nq + kColQuads - 1) / kColQuads), block(kColQuads * kGroups);
   const KernelRole role = p.G > 0 ? KernelRole::kLast : KernelRole::kOnly;
@@ -376,24 +571,68 @@ hipError_t launch_cols(const BwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+std::atomic<int> g_max_launches{1};   // sp_region_set_bwd_launches
+
+// Compute units of the device that runs `stream`, cached per device (0 if
+// unknown: the partials path is then taken).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus(hipStream_t stream) {
+  int dev = 0;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return 0;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return 0;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return 0;
+  int n = g_cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    g_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <class E, int VPT, bool DRES, bool DROP>
-hipError_t launch_stages(const BwdParams& p, const Shape& sh, hipStream_t stream) {
+hipError_t launch_rows(const BwdParams& p, const ColOut& o, int np, const Shape& sh, hipStream_t stream) {
   constexpr int MAXBS = SPR_BWD_MAX_THREADS;
-  constexpr int RING = ring_for<VPT, MAXBS, DROP>();
+  constexpr int RS = rows_in_flight<VPT, DRES, DROP>();
+  constexpr int RR = ring_rows<VPT, DRES, DROP>();
   const dim3 grid(static_cast<unsigned>(p.G)), block(sh.threads);
-  launch_kernel(sp_region_bwd_rows_kernel<E, VPT, RING, DRES, DROP, MAXBS>, grid, block, stream, KernelRole::kFirst, p);
+  const int64_t rows_per_block = (p.T + p.G - 1) / p.G;
+  if constexpr (!DROP) {
+    // The direct path when the row blocks are short enough and every block
+    // of the launch can be resident at once (measured at s = h = 4096, t =
+    // 8, 512 local tokens: 128 row + 128 column blocks, 9.2 us against
+    // 15.9 us for the partials path).
+    constexpr int RD = RS < 4 ? RS : 4;
+    const int gcols = (p.h / E::kVec + kDirectLanes - 1) / kDirectLanes;
+    if (g_max_launches.load(std::memory_order_relaxed) == 1 && rows_per_block <= RD && p.G <= kDirectMaxBlocks &&
+        p.G + gcols <= device_cus(stream)) {
+      launch_kernel(sp_region_bwd_direct_kernel<E, VPT, RD, DRES, MAXBS>, dim3(static_cast<unsigned>(p.G + gcols)),
+                    block, stream, KernelRole::kOnly, p, o);
+      return hipGetLastError();
+    }
+  }
+  if (rows_per_block <= RS)
+    launch_kernel(sp_region_bwd_rows_kernel<E, VPT, RS, true, DRES, DROP, MAXBS>, grid, block, stream,
+                  KernelRole::kFirst, p);
+  else
+    launch_kernel(sp_region_bwd_rows_kernel<E, VPT, RR, false, DRES, DROP, MAXBS>, grid, block, stream,
+                  KernelRole::kFirst, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_cols(p, stream);
+  return launch_cols(p, o, np, stream);
 }
 
 template <class E, bool DROP>
-hipError_t launch_rows(const BwdParams& p, const Shape& sh, hipStream_t stream) {
+hipError_t launch_e(const BwdParams& p, const ColOut& o, int np, const Shape& sh, hipStream_t stream) {
   const bool dres = p.dres != nullptr;
   switch (sh.vpt) {
-    case 1: return dres ? launch_stages<E, 1, true, DROP>(p, sh, stream) : launch_stages<E, 1, false, DROP>(p, sh, stream);
-    case 2: return dres ? launch_stages<E, 2, true, DROP>(p, sh, stream) : launch_stages<E, 2, false, DROP>(p, sh, stream);
-    case 4: return dres ? launch_stages<E, 4, true, DROP>(p, sh, stream) : launch_stages<E, 4, false, DROP>(p, sh, stream);
+    case 1: return dres ? launch_rows<E, 1, true, DROP>(p, o, np, sh, stream) : launch_rows<E, 1, false, DROP>(p, o, np, sh, stream);
+    case 2: return dres ? launch_rows<E, 2, true, DROP>(p, o, np, sh, stream) : launch_rows<E, 2, false, DROP>(p, o, np, sh, stream);
+    case 4: return dres ? launch_rows<E, 4, true, DROP>(p, o, np, sh, stream) : launch_rows<E, 4, false, DROP>(p, o, np, sh, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -407,25 +646,36 @@ Shape bwd_shape(int h, int dtype) {
   const int nvec = h / vec;
   for (int vpt : {1, 2, 4}) {
     const int need = (nvec + vpt - 1) / vpt;
-    if (need <= SPR_BWD_MAX_THREADS) return Shape{vpt, ((need + 63) / 64) * 64};
+    if (need <= SPR_BWD_MAX_THREADS) {
+      // At least kGroups * 2 threads: the reduction's (group, quad) layout.
+      const int t = ((need + 63) / 64) * 64;
+      return Shape{vpt, t < kGroups * 2 ? kGroups * 2 : t};
+    }
   }
   return Shape{0, 0};
 }
+
+void set_bwd_launches(int n) { g_max_launches.store(n, std::memory_order_relaxed); }
 
 hipError_t launch_bwd(const BwdParams& params, int dtype, hipStream_t stream) {
   BwdParams p = params;
   p.ws_sstride = ws_slot_stride(p.h);
   p.ws_bstride = ws_block_stride(p.h, p.nparts);
-  if (p.G > 0) {
-    const Shape sh = bwd_shape(p.h, dtype);
-    const bool drop = p.dpartial != nullptr;
-    if (dtype == 1) return drop ? launch_rows<Bf16, true>(p, sh, stream) : launch_rows<Bf16, false>(p, sh, stream);
-    return drop ? launch_rows<F32, true>(p, sh, stream) : launch_rows<F32, false>(p, sh, stream);
+  ColOut o{{p.dgamma, nullptr, nullptr}, 1, p.accumulate};
+  if (p.slot_dbeta > 0) o.p[o.np++] = p.dbeta;
+  if (p.slot_dbias > 0) o.p[o.np++] = p.dbias;
+  const int np = o.np;
+  if (p.G == 0) {
+    // No rows: every output is 0 (every group of partials is empty); an
+    // accumulating call adds nothing and launches nothing.
+    if (p.accumulate) return hipSuccess;
+    return launch_cols(p, o, np, stream);
   }
-  // No rows: every output is 0 (every group of partials is empty); an
-  // accumulating call adds nothing and launches nothing.
-  if (p.accumulate) return hipSuccess;
-  return launch_cols(p, stream);
+  const Shape sh = bwd_shape(p.h, dtype);
+  if (sh.vpt == 0) return hipErrorInvalidValue;
+  const bool drop = p.dpartial != nullptr;
+  if (dtype == 1) return drop ? launch_e<Bf16, true>(p, o, np, sh, stream) : launch_e<Bf16, false>(p, o, np, sh, stream);
+  return drop ? launch_e<F32, true>(p, o, np, sh, stream) : launch_e<F32, false>(p, o, np, sh, stream);
 }
 
 }  // namespace spr

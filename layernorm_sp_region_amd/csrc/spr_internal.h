@@ -121,10 +121,13 @@ inline int64_t ws_round(int64_t floats) {
 }
 inline int64_t ws_slot_stride(int64_t h) { return ws_round(h); }
 inline int64_t ws_block_stride(int64_t h, int nslots) { return ws_round(nslots * ws_slot_stride(h)); }
+// Whole workspace: the G blocks' partials.
+inline int64_t ws_total_bytes(int64_t G, int64_t h, int nslots) { return G * ws_block_stride(h, nslots) * 4; }
 
 // Launchers: return hipSuccess or the launch error.  `dtype` 0 = f32, 1 = bf16.
 hipError_t launch_fwd(const FwdParams& p, int dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int dtype, hipStream_t stream);
+void set_bwd_launches(int n);   // 1: one launch on small shards (default); 2: always the partials' two
 hipError_t launch_copy(const void* src, void* dst, size_t nbytes, hipStream_t stream);
 
 // Launch shapes (exposed for tests of the host logic).

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.sp_region_abi_version() == spr.ABI_VERSION == 3
+    assert lib.sp_region_abi_version() == spr.ABI_VERSION == 4
     for st in range(6):
         assert lib.sp_region_strerror(st)
     assert lib.sp_region_strerror(99) == b"unknown status"

@@ -378,3 +378,106 @@ def test_slab_pointer_table_matches_strided(cuda_device, name):
                rstd=to_np_f64(b.rstd), mask=b.mask.cpu().numpy(), dx=to_np_f64(g.dx), dgamma=to_np_f64(g.dgamma),
                dbeta=None if g.dbeta is None else to_np_f64(g.dbeta))
     compare(w, inp, gpu, w.t - 1)
+
+
+# On small shards the backward is one launch whose column blocks sum
+# dgamma/dbeta straight from dy and z (tiny, page_demo and the "direct"
+# cases: at most 4 rows per row block, a ragged last vector of columns, dres,
+# RMSNorm, a single row); otherwise, and always under set_bwd_launches(2),
+# row blocks write partial sums and a second launch reduces them.  Both must
+# give the same bits.
+LAUNCH_CASES = ["tiny", "page_demo", "shard70b", "ragged13b",
+                W.custom("wide_h16384_dres", h=16384, t=4, s=4 * 40, p_drop=0.2),
+                W.custom("f32_h5120_rms_t3", h=5120, t=3, s=3 * 50, dtype="f32", norm="rmsnorm", p_drop=0.0,
+                         bias=False),
+                W.custom("direct_bf16_h4104_t2_dres", h=4104, t=2, s=2 * 50, p_drop=0.1),
+                W.custom("direct_rms_f32_h2048", h=2048, t=4, s=4 * 37, dtype="f32", norm="rmsnorm", p_drop=0.0,
+                         bias=False),
+                W.custom("direct_one_row_bf16", h=1024, t=2, s=2, p_drop=0.1)]
+
+
+@pytest.mark.parametrize("case", LAUNCH_CASES, ids=[c if isinstance(c, str) else c.name for c in LAUNCH_CASES])
+def test_backward_launch_paths_bitwise_equal(cuda_device, case):
+    import torch
+    w = W.BY_NAME[case] if isinstance(case, str) else case
+    inp = inputs_for(w) if isinstance(case, str) else W.make_inputs(w)
+    log(f"[launch-paths] {w.name}")
+    t = lambda a: W.as_torch(a, cuda_device)
+    fo = spr.fwd(t(inp["partials"]), t(inp["gamma"]), t(inp["beta"]), bias=t(inp["bias"]),
+                 residual=t(inp["residual"]), b=inp["b"], s=inp["s"], t=w.t, rank=1, eps=w.eps, p_drop=w.p_drop,
+                 seed=inp["seed"], norm=w.norm, cu_seqlens=inp["cu_seqlens"])
+    dres = t(W.make_inputs(w, seed=77)["dy"]) if "dres" in w.name else None
+    kw = dict(b=inp["b"], s=inp["s"], t=w.t, norm=w.norm, dres_in=dres)
+    dkw = dict(kw, rank=1, p_drop=w.p_drop, seed=inp["seed"], cu_seqlens=inp["cu_seqlens"],
+               want_dbias=inp["bias"] is not None)
+    # One workspace for every call, read by ordinary kernels in between (so
+    # stale copies of its lines sit in the L2 caches when the next call
+    # reuses it), and the default path run twice.
+    T, h = fo.z.shape
+    ws = torch.zeros(spr.dropout_workspace_bytes(T, h), dtype=torch.uint8, device=cuda_device)
+    outs = {}
+    try:
+        for n in (2, 1, 1):
+            spr.set_bwd_launches(n)
+            g = spr.bwd(t(inp["dy"]), fo.z, fo.mean, fo.rstd, t(inp["gamma"]), workspace=ws, **kw)
+            float(ws.float().sum())
+            d = spr.bwd_dropout(t(inp["dy"]), fo.z, fo.mean, fo.rstd, t(inp["gamma"]), workspace=ws, **dkw)
+            float(ws.float().sum())
+            torch.cuda.synchronize()
+            if n in outs:
+                outs[3] = (g, d)
+            else:
+                outs[n] = (g, d)
+    finally:
+        spr.set_bwd_launches(1)
+    for a, b in zip(outs[1], outs[3]):
+        for k in a._fields:
+            x, y = getattr(a, k), getattr(b, k)
+            if x is not None:
+                assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), k + " (one launch, repeated)"
+    for a, b in zip(outs[1], outs[2]):
+        for k in a._fields:
+            x, y = getattr(a, k), getattr(b, k)
+            if x is None:
+                assert y is None, k
+                continue
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), k
+    with pytest.raises(spr.SpRegionError):
+        spr.set_bwd_launches(3)
+
+
+@pytest.mark.parametrize("launches", [1, 2])
+def test_backward_reads_rewritten_inputs(cuda_device, launches):
+    """The backward reads z, dy and its workspace as the previous kernels left
+    them, although other kernels read the same memory (so L2 copies of the old
+    contents exist) before it was rewritten: shard B's results must not carry
+    any of shard A's values.  A 512 x 4096 shard (4 MB tensors, the size of
+    one L2) and the same output and workspace buffers for both shards."""
+    import torch
+    wa = W.BY_NAME["page_demo"]
+    wb = W.custom("page_demo_b", h=4096, t=8, s=4096, p_drop=0.1, bias=False, seed=123)
+    ia, ib = inputs_for(wa), W.make_inputs(wb)
+    t = lambda a: W.as_torch(a, cuda_device)
+    T, h = ia["T"], wa.h
+    out = spr.FwdOut(*(torch.empty((T, h), dtype=torch.bfloat16, device=cuda_device) for _ in range(2)),
+                     torch.empty(T, device=cuda_device), torch.empty(T, device=cuda_device), None)
+    dy = torch.empty((T, h), dtype=torch.bfloat16, device=cuda_device)
+    ws = torch.zeros(spr.workspace_bytes(T, h), dtype=torch.uint8, device=cuda_device)
+    bo = spr.BwdOut(torch.empty((T, h), dtype=torch.bfloat16, device=cuda_device), torch.empty(h, device=cuda_device),
+                    torch.empty(h, device=cuda_device))
+    kw = dict(b=1, s=4096, t=8, rank=2, eps=1e-5, p_drop=0.1, norm="layernorm")
+    try:
+        spr.set_bwd_launches(launches)
+        for inp in (ia, ib):
+            spr.fwd(t(inp["partials"]), t(inp["gamma"]), t(inp["beta"]), residual=t(inp["residual"]),
+                    seed=inp["seed"], out=out, **kw)
+            dy.copy_(t(inp["dy"]))
+            spr.bwd(dy, out.z, out.mean, out.rstd, t(inp["gamma"]), b=1, s=4096, t=8, workspace=ws, out=bo)
+            # Ordinary kernels read every buffer the next shard rewrites.
+            float(out.z.float().sum() + dy.float().sum() + ws.float().sum() + bo.dx.float().sum())
+        torch.cuda.synchronize()
+    finally:
+        spr.set_bwd_launches(1)
+    gpu = dict(z=to_np_bits(out.z), y=to_np_f64(out.y), mean=to_np_f64(out.mean), rstd=to_np_f64(out.rstd),
+               mask=None, dx=to_np_f64(bo.dx), dgamma=to_np_f64(bo.dgamma), dbeta=to_np_f64(bo.dbeta))
+    compare(wb, ib, gpu, 2)
