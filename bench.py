@@ -223,6 +223,176 @@ def cpu_baseline_parallel(w, T, budget_s=12.0, chunk=64, max_procs=16):
 
 
 # ---------------------------------------------------------------------------
+# The other workloads of the configuration list, each measured like the
+# headline one (rotating sets, wall-clock steps, event-stamped kernel times)
+# plus a HIP-graph replay of the same steps (the small shards' wall clock is
+# bound by the host's per-call work, the replay by the GPU's).
+# ---------------------------------------------------------------------------
+CONFIGS = [("c1", "tiny"), ("c2", "page_demo"), ("c4", "ragged13b"), ("c5", "long128k")]
+
+
+def device_inputs(w, dev):
+    """Seeded inputs of a shard too large to draw on the host in a short run:
+    slabs, residual and dy drawn on the device (workloads.device_normal), the
+    [h] parameters from the host generator."""
+    import numpy as np
+    import workloads as W
+    T = w.b * w.s // w.t
+    dt = None if w.dtype == "bf16" else __import__("torch").float32
+    rng = np.random.default_rng(w.input_seed)
+    par = lambda x: W.as_torch(W._to_storage(x, w.dtype), dev)
+    return dict(b=w.b, s=w.s, T=T, cu_seqlens=None, seed=w.dropout_seed,
+                partials=W.device_normal((w.t, T, w.h), seed=101, device=dev, scale=w.slab_scale, dtype=dt),
+                residual=W.device_normal((1, T, w.h), seed=102, device=dev, dtype=dt)[0] if w.has_residual else None,
+                dy=W.device_normal((1, T, w.h), seed=103, device=dev, dtype=dt)[0],
+                bias=par(0.02 * rng.standard_normal(w.h)) if w.has_bias else None,
+                gamma=par(rng.uniform(0.5, 1.5, size=w.h)),
+                beta=par(0.1 * rng.standard_normal(w.h)) if w.has_beta else None)
+
+
+def cpu_full(w, inp, chunk=64, label=None):
+    """The oracle over every row of a shard once, one process."""
+    import numpy as np
+    import oracle.region as ref
+    T = inp["T"]
+    t0 = time.perf_counter()
+    for start in range(0, T, chunk):
+        rows = np.arange(start, min(T, start + chunk))
+        o = ref.region_forward(inp["partials"], t=w.t, rank=0, dtype=w.dtype, norm=w.norm, eps=w.eps,
+                               p_drop=w.p_drop, seed=inp["seed"], gamma=inp["gamma"], beta=inp["beta"],
+                               bias=inp["bias"], residual=inp["residual"], cu_seqlens=inp["cu_seqlens"], rows=rows)
+        ref.region_backward(inp["dy"][rows], o["z"], inp["gamma"], dtype=w.dtype, norm=w.norm, eps=w.eps)
+    el = time.perf_counter() - t0
+    return dict(value=T / el, unit="tokens/s", cores=1, kind="oracle", cpu=cpu_model(),
+                gbs=(fwd_bytes(w, T) + bwd_bytes(w, T)) / el / 1e9,
+                sample=label or f"all {T} rows of the shard once, in chunks of {chunk} ({el:.2f} s, single process)")
+
+
+def measure_config(w, inp, dev, steps, warmup, nsets):
+    """fwd + bwd steps of one workload whose tensors are on the device."""
+    import numpy as np
+    import torch
+    import layernorm_sp_region_amd as spr
+    T, h = inp["T"], w.h
+    to = lambda a: a if a is None or isinstance(a, torch.Tensor) else W_as_torch(a, dev)
+    gamma, beta, bias = to(inp["gamma"]), to(inp["beta"]), to(inp["bias"])
+    dt = gamma.dtype
+    ln = w.norm == "layernorm"
+    cu = torch.tensor(inp["cu_seqlens"], dtype=torch.int32, device=dev) if inp["cu_seqlens"] is not None else None
+    base = dict(P=to(inp["partials"]), res=to(inp["residual"]), dy=to(inp["dy"]))
+    sets = []
+    for i in range(nsets):
+        s = {k: (v if i == 0 or v is None else v.clone()) for k, v in base.items()}
+        P = spr.empty_partials(w.t, T, h, dt, dev)
+        P.copy_(s["P"])
+        s["P"] = P
+        s["fo"] = spr.FwdOut(torch.empty((T, h), dtype=dt, device=dev), torch.empty((T, h), dtype=dt, device=dev),
+                             torch.empty(T, device=dev) if ln else None, torch.empty(T, device=dev), None)
+        s["bo"] = spr.BwdOut(torch.empty((T, h), dtype=dt, device=dev), torch.empty(h, device=dev),
+                             torch.empty(h, device=dev) if ln else None)
+        sets.append(s)
+    del base
+    ws = torch.empty(max(16, spr.workspace_bytes(T, h)), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        s = sets[i % nsets]
+        if ev is not None:
+            spr.time_next_call(ev[0], ev[1])
+        fo = spr.fwd(s["P"], gamma, beta, bias=bias, residual=s["res"], b=inp["b"], s=inp["s"], t=w.t, rank=0,
+                     eps=w.eps, p_drop=w.p_drop, seed=inp["seed"], norm=w.norm, cu_seqlens=cu, out=s["fo"])
+        if ev is not None:
+            spr.time_next_call(ev[2], ev[3])
+        spr.bwd(s["dy"], fo.z, fo.mean, fo.rstd, gamma, b=inp["b"], s=inp["s"], t=w.t, norm=w.norm,
+                workspace=ws, out=s["bo"])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - t0) / steps * 1e6
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for e in evs:
+        for x in e:
+            x.record()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    fwd_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3)
+    bwd_us = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e3)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(nsets):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        for i in range(nsets):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // nsets)
+    t2 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t2) / (reps * nsets) * 1e6
+    del graph, sets, ws
+    fb, bb = fwd_bytes(w, T), bwd_bytes(w, T)
+    return {"workload": w.name, "local_tokens": T, "h": h, "dtype": w.dtype, "norm": w.norm, "steps": steps,
+            "rotating_sets": nsets, "step_us_wall": wall_us, "step_us_graph_replay": graph_us,
+            "fwd_us": fwd_us, "bwd_us": bwd_us,
+            "tokens_per_s_wall": T / (wall_us * 1e-6), "tokens_per_s_graph_replay": T / (graph_us * 1e-6),
+            "tokens_per_s_kernels": T / ((fwd_us + bwd_us) * 1e-6),
+            "fwd_bwd_pct_of_peak": 100 * (fb + bb) / ((fwd_us + bwd_us) * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "fwd_frac": fb / (fwd_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "bwd_gbs": bb / (bwd_us * 1e-6) / 1e9,
+            "algorithmic_bytes": {"fwd": fb, "bwd": bb}}
+
+
+def W_as_torch(a, dev):
+    import workloads as W
+    return W.as_torch(a, dev)
+
+
+def run_configs(args, dev):
+    import torch
+    import workloads as W
+    out = {}
+    for tag, name in CONFIGS:
+        w = W.BY_NAME[name]
+        t_gen = time.time()
+        big = name == "long128k"
+        inp = device_inputs(w, dev) if big else W.make_inputs(w)
+        steps = max(10, args.steps // 5) if big else args.steps
+        rec = measure_config(w, inp, dev, steps, max(2, args.warmup // 2), 1 if big else args.sets)
+        rec["inputs"] = ("seeded on-device draws (workloads.device_normal), [h] parameters from the host generator"
+                         if big else "workloads.make_inputs (host, seeded)")
+        if not args.no_cpu_baseline:
+            if big:
+                sub = W.custom(f"{name}_first2048rows", h=w.h, t=w.t, s=w.t * 2048, p_drop=w.p_drop, bias=w.has_bias,
+                               residual=w.has_residual, beta=w.has_beta)
+                sinp = W.make_inputs(sub)
+                rec["cpu_baseline"] = cpu_full(sub, sinp, label=f"a 2048-row sub-shard of the {inp['T']}-row shard "
+                                                                 f"(same h, t, p, norm), every row once, single process")
+                del sinp
+            elif name != "ragged13b":
+                rec["cpu_baseline"] = cpu_full(w, inp)
+        eprint(f"[bench] {tag} {name}: T={rec['local_tokens']} step {rec['step_us_wall']:.1f} us wall, "
+               f"{rec['step_us_graph_replay']:.1f} us graph replay; fwd {rec['fwd_us']:.1f} us "
+               f"(frac {rec['fwd_frac']:.3f}), bwd {rec['bwd_us']:.1f} us; {rec['fwd_bwd_pct_of_peak']:.1f}% of peak "
+               f"(inputs {time.time() - t_gen:.1f}s)")
+        out[tag] = rec
+        del inp
+        torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
 def run(args):
     import numpy as np
     import torch
@@ -404,6 +574,9 @@ def run(args):
 
     plan = plan_timing(W)
     traffic = read_traffic()
+    del sets, ws
+    torch.cuda.empty_cache()
+    configs = None if args.no_configs else run_configs(args, dev)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp)
     cpu_par = None if args.no_cpu_baseline else cpu_baseline_parallel(w, T)
     kernel_us = (fwd_ms.mean() + bwd_ms.mean()) * 1e3
@@ -441,6 +614,7 @@ def run(args):
         "cpu_baseline": cpu,
         "cpu_baseline_parallel": cpu_par,
         "host_planning": plan,
+        "configs": configs,
     }
     print(json.dumps(rec), flush=True)
 
@@ -527,6 +701,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the p = 0 forward and the warm one-set passes (they launch the step's kernels "
                          "again, so a profiler's per-kernel averages would mix them in)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (c1 tiny, c2 page_demo, c4 ragged13b, c5 long128k)")
     ap.add_argument("--summarize-rocprof", metavar="DIR")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
