@@ -22,8 +22,8 @@
 // reads back only what it wrote, so no barrier), in registers for shorter
 // rows -- for the statistics (a second pass) and the y phase, which fetches
 // gamma/beta one slot ahead.  Wave sums use DPP row steps plus readlane;
-// two-wave rows (WPR = 2, h above 8192 bf16) combine their two sums through
-// LDS in wave order.  Every memory instruction is unconditional (see the
+// rows of several waves (WPR = 2 for h above 8192 bf16; 2 or 4 on shards of
+// at most 1024 rows) combine their sums through LDS in wave order.  Every memory instruction is unconditional (see the
 // kernel), and row base pointers are wave-uniform (SGPR + 32-bit lane
 // offsets).  Slabs and residual use nontemporal loads; gamma, beta and bias
 // (read by every row) ordinary cached loads.
@@ -315,8 +315,24 @@ hipError_t launch_ns(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Shards of at most kSplitRows rows: one wave per row would fill at most
+// 256 blocks of 4 waves, and latency, not bandwidth, bounds the call.  Their
+// rows get 4 waves (2 for rows of 2 vectors per lane) with the same
+// vectors split between them (measured at 512 x 4096 bf16: 12.9 -> 11.0 us).
+#ifndef SPR_FWD_SPLIT_T
+#define SPR_FWD_SPLIT_T 1024
+#endif
+constexpr int64_t kSplitRows = SPR_FWD_SPLIT_T;
 template <class E>
 hipError_t launch_e(const FwdParams& p, const Shape& sh, hipStream_t stream) {
+  if (sh.threads == 64 && p.T <= kSplitRows) {
+    switch (sh.vpt) {
+      case 2: return launch_ns<E, 1, 2>(p, stream);
+      case 4: return launch_ns<E, 1, 4>(p, stream);
+      case 8: return launch_ns<E, 2, 4>(p, stream);
+      default: break;
+    }
+  }
   if (sh.threads == 64) {
     switch (sh.vpt) {
       case 1: return launch_ns<E, 1, 1>(p, stream);

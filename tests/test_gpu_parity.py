@@ -303,7 +303,9 @@ def test_oracle_philox_matches_rocrand_host_generator(cuda_device):
 
 # Every forward slot count (1, 2, 4, 8, 10, 12, 14, 16 vectors per lane, and
 # two waves per row) in both dtypes, against the oracle, with ragged and
-# uniform shards, both norms, with and without dropout/bias/residual.
+# uniform shards, both norms, with and without dropout/bias/residual.  Shards
+# of at most 1024 rows split rows of 2, 4 and 8 vectors per lane over 2 or 4
+# waves; the last three shapes keep one wave per row (more than 1024 rows).
 SLOT_SHAPES = [
     # (h, dtype, norm, t, T-or-lengths, p, bias, residual)
     (64, "bf16", "layernorm", 3, 21, 0.3, True, True),           # 8 vectors: 1 slot
@@ -316,6 +318,9 @@ SLOT_SHAPES = [
     (3072, "f32", "rmsnorm", 4, (8, 4), 0.4, False, True),       # 768 vectors: 12 slots, ragged
     (3584, "f32", "layernorm", 2, 7, 0.0, True, False),          # 896 vectors: 14 slots
     (4100, "f32", "layernorm", 1, 5, 0.2, False, True),          # 1025 vectors: two waves per row
+    (1024, "bf16", "layernorm", 2, 1100, 0.1, True, True),       # 128 vectors: 2 slots, one wave per row
+    (1024, "f32", "rmsnorm", 2, 1030, 0.2, False, True),         # 256 vectors: 4 slots, one wave per row
+    (4096, "bf16", "layernorm", 2, 1040, 0.1, False, True),      # 512 vectors: 8 slots, one wave per row
 ]
 
 
