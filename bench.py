@@ -673,7 +673,8 @@ def traffic_summary(fetch_dir, write_dir, copy_bytes=1 << 30):
     fwd = None
     # One line per kernel instantiation (the rows kernel with and without the
     # dropout backward are different kernels), in the order of the path.
-    order = ("sp_region_fwd_kernel", "sp_region_bwd_rows_kernel", "sp_region_bwd_cols_kernel")
+    order = ("sp_region_fwd_kernel", "sp_region_bwd_rows_kernel", "sp_region_bwd_cols_kernel",
+             "sp_region_bwd_direct_kernel")
     names = sorted((k for k in fe if any(o in k for o in order) and k in wr),
                    key=lambda k: (next(i for i, o in enumerate(order) if o in k), k))
     for key in names:
