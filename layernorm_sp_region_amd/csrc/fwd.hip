@@ -22,10 +22,10 @@
 // reads back only what it wrote, so no barrier), in registers for shorter
 // rows -- for the statistics (a second pass) and the y phase, which fetches
 // gamma/beta one slot ahead.  Wave sums use DPP row steps plus readlane;
-// rows of several waves (WPR = 2 for h above 8192 bf16; 2 or 4 on shards of
-// at most 1024 rows) combine their sums through LDS in wave order.  Every memory instruction is unconditional (see the
-// kernel), and row base pointers are wave-uniform (SGPR + 32-bit lane
-// offsets).  Slabs and residual use nontemporal loads; gamma, beta and bias
+// rows of several waves (WPR = 2 for h above 8192 bf16; 4 on shards of at
+// most 1024 rows) combine their sums through LDS in wave order.  Every
+// memory instruction is unconditional (see the kernel), and row base
+// pointers are wave-uniform (SGPR + 32-bit lane offsets).  Slabs and residual use nontemporal loads; gamma, beta and bias
 // (read by every row) ordinary cached loads.
 #include "spr_device.h"
 #include "spr_internal.h"
@@ -38,7 +38,15 @@ namespace {
 #ifndef SPR_FWD_LOOP
 #define SPR_FWD_LOOP 0
 #endif
-constexpr int kRowsPerBlockW1 = 4;   // WPR = 1: four independent rows per block
+// WPR = 1: independent rows per block.  One: every wave is a block of its
+// own, so the dispatcher hands rows to compute units one at a time as they
+// free up and the last generation of blocks ends evenly (measured against 4
+// rows per block: ragged13b 80.5 -> 76.4 us, long128k 537.1 -> 531.7 us, the
+// 70B shard 66.5 -> 66.0 us in the step).
+#ifndef SPR_FWD_ROWS_PER_BLOCK
+#define SPR_FWD_ROWS_PER_BLOCK 1
+#endif
+constexpr int kRowsPerBlockW1 = SPR_FWD_ROWS_PER_BLOCK;
 
 // Sum over the WPR waves of a row, in wave order (uniform result).
 template <int WPR>
@@ -315,10 +323,11 @@ hipError_t launch_ns(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Shards of at most kSplitRows rows: one wave per row would fill at most
-// 256 blocks of 4 waves, and latency, not bandwidth, bounds the call.  Their
-// rows get 4 waves (2 for rows of 2 vectors per lane) with the same
-// vectors split between them (measured at 512 x 4096 bf16: 12.9 -> 11.0 us).
+// Shards of at most kSplitRows rows: one wave per row would leave most of
+// the 1024 SIMDs idle, and latency, not bandwidth, bounds the call.  Their
+// rows of 4 or 8 vectors per lane get 4 waves, the vectors split between
+// them (measured at 512 x 4096 bf16: 11.9 -> 10.8 us; rows of 2 vectors per
+// lane on 2 waves measured no better at 64 x 512 fp32).
 #ifndef SPR_FWD_SPLIT_T
 #define SPR_FWD_SPLIT_T 1024
 #endif
@@ -327,7 +336,6 @@ template <class E>
 hipError_t launch_e(const FwdParams& p, const Shape& sh, hipStream_t stream) {
   if (sh.threads == 64 && p.T <= kSplitRows) {
     switch (sh.vpt) {
-      case 2: return launch_ns<E, 1, 2>(p, stream);
       case 4: return launch_ns<E, 1, 4>(p, stream);
       case 8: return launch_ns<E, 2, 4>(p, stream);
       default: break;

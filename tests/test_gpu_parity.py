@@ -304,8 +304,8 @@ def test_oracle_philox_matches_rocrand_host_generator(cuda_device):
 # Every forward slot count (1, 2, 4, 8, 10, 12, 14, 16 vectors per lane, and
 # two waves per row) in both dtypes, against the oracle, with ragged and
 # uniform shards, both norms, with and without dropout/bias/residual.  Shards
-# of at most 1024 rows split rows of 2, 4 and 8 vectors per lane over 2 or 4
-# waves; the last three shapes keep one wave per row (more than 1024 rows).
+# of at most 1024 rows split rows of 4 and 8 vectors per lane over 4 waves;
+# the last three shapes keep one wave per row (more than 1024 rows).
 SLOT_SHAPES = [
     # (h, dtype, norm, t, T-or-lengths, p, bias, residual)
     (64, "bf16", "layernorm", 3, 21, 0.3, True, True),           # 8 vectors: 1 slot
