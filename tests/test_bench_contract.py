@@ -59,3 +59,16 @@ def test_bench_prints_one_contract_line(cuda_device):
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-12
     assert rec["cpu_baseline"] is None and rec["extras"] is None
+    # The other workloads of the configuration list, each with its own step,
+    # kernel times and fractions of peak.
+    cfg = rec["configs"]
+    assert sorted(cfg) == ["c1", "c2", "c4", "c5"]
+    names = {"c1": "tiny", "c2": "page_demo", "c4": "ragged13b", "c5": "long128k"}
+    for tag, c in cfg.items():
+        assert c["workload"] == names[tag] and c["local_tokens"] > 0
+        for key in ("step_us_wall", "step_us_graph_replay", "fwd_us", "bwd_us", "tokens_per_s_wall",
+                    "tokens_per_s_kernels", "fwd_bwd_pct_of_peak", "fwd_frac"):
+            assert c[key] > 0, (tag, key)
+        assert abs(c["tokens_per_s_kernels"] - c["local_tokens"] / ((c["fwd_us"] + c["bwd_us"]) * 1e-6)) < 1e-6 * c[
+            "tokens_per_s_kernels"]
+        assert "cpu_baseline" not in c
