@@ -228,10 +228,21 @@ __device__ __forceinline__ void finish_rows(const BwdParams& p, ColSums<VPT, E::
   for (int j = 0; j < N; ++j) {
     const int li = li0 + j;
     if (li >= r1) continue;   // block-uniform
-    float s1 = slot[0][j][0], s2 = slot[1][j][0];
-    for (int w = 1; w < nwaves; ++w) {   // wave order: the same total in every thread
-      s1 += slot[0][j][w];
-      s2 += slot[1][j][w];
+    // Wave order: the same total in every thread.  Every wave slot's LDS
+    // read is issued before the adds (the slots past nwaves are read and
+    // not added), rather than one read per add.
+    constexpr int kMaxWaves = SPR_BWD_MAX_THREADS / kWave;
+    float a1[kMaxWaves], a2[kMaxWaves];
+#pragma unroll
+    for (int w = 0; w < kMaxWaves; ++w) {
+      a1[w] = slot[0][j][w];
+      a2[w] = slot[1][j][w];
+    }
+    float s1 = a1[0], s2 = a2[0];
+#pragma unroll
+    for (int w = 1; w < kMaxWaves; ++w) {
+      s1 = w < nwaves ? s1 + a1[w] : s1;
+      s2 = w < nwaves ? s2 + a2[w] : s2;
     }
     const float c1 = ln ? s1 * inv_h : 0.0f;
     const float c2 = s2 * inv_h;
