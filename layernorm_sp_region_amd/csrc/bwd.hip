@@ -50,11 +50,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const char* row, int 
 __device__ __forceinline__ u32x4 ld16_row(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kCpolNontemporal));
 }
-// Nontemporal store (measured: the next kernel no longer pays for writing
-// back dirty dx lines).
-__device__ __forceinline__ void st16_dx(void* p, u32x4 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-}
 
 #ifndef SPR_BWD_MAX_THREADS
 #define SPR_BWD_MAX_THREADS 512   // block size cap of the row stage
@@ -270,7 +265,9 @@ __device__ __forceinline__ void finish_rows(const BwdParams& p, ColSums<VPT, E::
 #pragma unroll
         for (int e = 0; e < V; ++e) dx[e] += f[e];
       }
-      st16_dx(static_cast<char*>(p.dx) + off + cs.vv[k] * 16, pack(E{}, dx));
+      // Nontemporal (measured: the next kernel no longer pays for writing
+      // back dirty dx lines).
+      st16_stream(static_cast<char*>(p.dx) + off + cs.vv[k] * 16, pack(E{}, dx));
       if constexpr (DROP) {
         // Through the dropout: kept channels times the forward's scale, the
         // forward's own mask (same seed, same global token).
@@ -286,7 +283,7 @@ __device__ __forceinline__ void finish_rows(const BwdParams& p, ColSums<VPT, E::
         }
 #pragma unroll
         for (int e = 0; e < V; ++e) cs.dbs[k][e] += dp[e];
-        st16_dx(static_cast<char*>(p.dpartial) + off + cs.vv[k] * 16, pack(E{}, dp));
+        st16_stream(static_cast<char*>(p.dpartial) + off + cs.vv[k] * 16, pack(E{}, dp));
       }
     }
   }

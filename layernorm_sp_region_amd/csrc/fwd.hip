@@ -26,7 +26,13 @@
 // most 1024 rows) combine their sums through LDS in wave order.  Every
 // memory instruction is unconditional (see the kernel), and row base
 // pointers are wave-uniform (SGPR + 32-bit lane offsets).  Slabs and residual use nontemporal loads; gamma, beta and bias
-// (read by every row) ordinary cached loads.
+// (read by every row) ordinary cached loads.  z and y take ordinary stores,
+// except on shards whose z and y together exceed the 256 MB Infinity Cache:
+// there y is stored nontemporally (YNT), so its lines stream to memory instead
+// of evicting dirty data through the caches (measured on the 128K-token
+// shard: step 669 -> 631 us; on the 70B shard, whose 67 MB of z and y fit,
+// the forward was 1 us slower with it).  z always keeps ordinary stores: the
+// backward reads it back (nontemporal z as well: 70B step 97.7 us).
 #include "spr_device.h"
 #include "spr_internal.h"
 
@@ -74,7 +80,7 @@ struct Slot {
 
 // At least 2 waves per SIMD: 8 rows per CU, which keeps a 2048-row shard
 // resident in one pass (the register budget caps how far loads are hoisted).
-template <class E, int NS, int VPL, int WPR, bool MASK>
+template <class E, int NS, int VPL, int WPR, bool MASK, bool YNT>
 __global__ __launch_bounds__(WPR == 1 ? 64 * kRowsPerBlockW1 : 64 * WPR, 2) void sp_region_fwd_kernel(const FwdParams p) {
   constexpr int V = E::kVec;
   constexpr int EB = 16 / V;
@@ -279,7 +285,8 @@ __global__ __launch_bounds__(WPR == 1 ? 64 * kRowsPerBlockW1 : 64 * WPR, 2) void
     }
 #pragma unroll
     for (int e = 0; e < V; ++e) yv[e] = __builtin_fmaf((zf[e] - mean) * rstd, gm[e], bt[e]);
-    st16(static_cast<char*>(p.y) + row_off + lane_off(k), pack(E{}, yv));
+    if constexpr (YNT) st16_stream(static_cast<char*>(p.y) + row_off + lane_off(k), pack(E{}, yv));
+    else st16(static_cast<char*>(p.y) + row_off + lane_off(k), pack(E{}, yv));
   };
   if constexpr (LOOP) {
 #pragma unroll 1
@@ -305,16 +312,29 @@ __global__ __launch_bounds__(WPR == 1 ? 64 * kRowsPerBlockW1 : 64 * WPR, 2) void
   }
 }
 
+// Shards whose z and y exceed this many bytes store y nontemporally (rows
+// of 8 or more vectors per lane; the mask-writing test path never).
+constexpr int64_t kStreamYBytes = int64_t{256} << 20;
+
 template <class E, int VPL, int WPR>
 hipError_t launch_ns(const FwdParams& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(WPR == 1 ? (p.T + kRowsPerBlockW1 - 1) / kRowsPerBlockW1 : p.T));
   const dim3 block(WPR == 1 ? 64 * kRowsPerBlockW1 : 64 * WPR);
   const bool mask = p.mask != nullptr;
+  const bool ynt = VPL >= 8 && !mask && 2 * p.T * p.h * (16 / E::kVec) > kStreamYBytes;
   switch (p.t) {
 #define SPR_NS(N)                                                                                          \
   case N:                                                                                                  \
-    if (mask) launch_kernel(sp_region_fwd_kernel<E, N, VPL, WPR, true>, grid, block, stream, KernelRole::kOnly, p); \
-    else launch_kernel(sp_region_fwd_kernel<E, N, VPL, WPR, false>, grid, block, stream, KernelRole::kOnly, p);     \
+    if (mask)                                                                                              \
+      launch_kernel(sp_region_fwd_kernel<E, N, VPL, WPR, true, false>, grid, block, stream, KernelRole::kOnly, p); \
+    else if constexpr (VPL >= 8) {                                                                         \
+      if (ynt)                                                                                             \
+        launch_kernel(sp_region_fwd_kernel<E, N, VPL, WPR, false, true>, grid, block, stream, KernelRole::kOnly, p); \
+      else                                                                                                 \
+        launch_kernel(sp_region_fwd_kernel<E, N, VPL, WPR, false, false>, grid, block, stream, KernelRole::kOnly, p); \
+    } else {                                                                                               \
+      launch_kernel(sp_region_fwd_kernel<E, N, VPL, WPR, false, false>, grid, block, stream, KernelRole::kOnly, p); \
+    }                                                                                                      \
     break;
     SPR_NS(1) SPR_NS(2) SPR_NS(3) SPR_NS(4) SPR_NS(5) SPR_NS(6) SPR_NS(7) SPR_NS(8)
 #undef SPR_NS

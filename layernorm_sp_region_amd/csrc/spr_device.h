@@ -32,6 +32,12 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Output no kernel of this library reads back: nontemporal, so its lines
+// stream to memory instead of filling the caches with dirty data.
+__device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 // 16 bytes -> float32 channels (bf16 widening is exact: the 16 bits become
 // the high half of the float32 pattern).
 __device__ __forceinline__ void unpack(Bf16, u32x4 v, float* f) {

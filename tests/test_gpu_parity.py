@@ -178,6 +178,28 @@ def test_long_context_parity_sampled_rows(cuda_device):
     _INPUTS.clear()
 
 
+def test_streamed_y_on_large_outputs(cuda_device):
+    """A shard whose z and y together pass 256 MB (4112 rows at the widest bf16
+    h, two waves per row) takes the forward variant that stores y
+    nontemporally: z bit-exact and y/statistics within the bars on sampled
+    rows against the oracle, and z/y bit for bit those of the mask-writing
+    variant (ordinary stores) on every row."""
+    import torch
+    w = W.custom("h16384_t2_streamed_y", h=16384, t=2, s=2 * 4112, p_drop=0.1)
+    assert 2 * 4112 * 16384 * 2 > 256 << 20
+    log("[parity] h16384_t2_streamed_y rank=1 mask=False (streamed y) and mask=True")
+    inp = inputs_for(w)
+    gpu = run_gpu(inp, w, 1, cuda_device, return_mask=False)
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([[0, 1, inp["T"] // 2, inp["T"] - 1], rng.integers(0, inp["T"], 28)]))
+    compare(w, inp, gpu, 1, rows=rows)
+    ref_gpu = run_gpu(inp, w, 1, cuda_device, return_mask=True)
+    assert np.array_equal(gpu["z"], ref_gpu["z"])
+    assert np.array_equal(gpu["y"], ref_gpu["y"])
+    torch.cuda.empty_cache()
+    _INPUTS.clear()
+
+
 EDGE = [
     # odd t, a partial last wave of vectors (h = 520 bf16 -> 65 vectors), b > 1
     (W.custom("odd_t3_h520", h=520, t=3, s=3 * 37, b=2, p_drop=0.25), 2, {}),
