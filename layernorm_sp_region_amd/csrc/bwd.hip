@@ -16,10 +16,10 @@
 // their dgamma/dbeta (/dbias) running sums in registers across rows.  A
 // block of at most R rows loads them all at once and takes ONE barrier for
 // their row sums; longer blocks stream rows through a ring.  (At the 70B
-// shard, 8 rows per block, both forms measure the same: 24.5-25.0 us for the
-// rows kernel against 24.3 us for a ring of 4 with a barrier per row,
-// rocprofv3; the one-barrier form is what the one-launch small-shard path is
-// built on.)
+// shard, 8 rows per block, the two forms measured the same, 24.5-25.0 us for
+// the rows kernel against 24.3 us for a ring of 4 with a barrier per row
+// (rocprofv3), before the row sums' LDS reads were batched (now 23.2 us); the
+// one-barrier form is what the one-launch small-shard path is built on.)
 //
 // Column sums, in one fixed tree whatever the path, so results are bitwise
 // reproducible: row block b's rows in row order; 32 groups of blocks (g,
