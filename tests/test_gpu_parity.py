@@ -178,16 +178,17 @@ def test_long_context_parity_sampled_rows(cuda_device):
     _INPUTS.clear()
 
 
-def test_streamed_y_on_large_outputs(cuda_device):
-    """A shard whose z and y together pass 256 MB (4112 rows at the widest bf16
-    h, two waves per row) takes the forward variant that stores y
-    nontemporally: z bit-exact and y/statistics within the bars on sampled
-    rows against the oracle, and z/y bit for bit those of the mask-writing
-    variant (ordinary stores) on every row."""
+@pytest.mark.parametrize("h,T,dtype", [(16384, 4112, "bf16"), (4096, 8200, "f32")])
+def test_streamed_y_on_large_outputs(cuda_device, h, T, dtype):
+    """A shard whose z and y together pass 256 MB takes the forward variant
+    that stores y nontemporally (bf16 at the widest h: two waves per row;
+    float32 at h = 4096: one wave of 16 slots): z bit-exact and y/statistics
+    within the bars on sampled rows against the oracle, and z/y bit for bit
+    those of the mask-writing variant (ordinary stores) on every row."""
     import torch
-    w = W.custom("h16384_t2_streamed_y", h=16384, t=2, s=2 * 4112, p_drop=0.1)
-    assert 2 * 4112 * 16384 * 2 > 256 << 20
-    log("[parity] h16384_t2_streamed_y rank=1 mask=False (streamed y) and mask=True")
+    w = W.custom(f"h{h}_t2_{dtype}_streamed_y", h=h, t=2, s=2 * T, p_drop=0.1, dtype=dtype)
+    assert 2 * T * h * (2 if dtype == "bf16" else 4) > 256 << 20
+    log(f"[parity] {w.name} rank=1 mask=False (streamed y) and mask=True")
     inp = inputs_for(w)
     gpu = run_gpu(inp, w, 1, cuda_device, return_mask=False)
     rng = np.random.default_rng(12)
