@@ -289,6 +289,25 @@ def test_copy_rejects(lib):
     assert lib.sp_region_hbm_copy(None, None, 0, None) == spr.SPR_OK
 
 
+def test_python_layer_rejects_host_tensors():
+    # The C entry points take raw device pointers and cannot tell host memory
+    # from device memory; the binding refuses CPU tensors before any call.
+    import torch
+    T, h, t = 8, 64, 2
+    P = torch.zeros(t, T, h)
+    g = torch.ones(h)
+    with pytest.raises(ValueError):
+        spr.fwd(P, g, g, b=1, s=t * T, t=t, rank=0, eps=1e-5, p_drop=0.0, seed=1)
+    with pytest.raises(ValueError):
+        spr.fwd([P[0], P[1]], g, g, b=1, s=t * T, t=t, rank=0, eps=1e-5, p_drop=0.0, seed=1)
+    z = torch.zeros(T, h)
+    st = torch.ones(T)
+    with pytest.raises(ValueError):
+        spr.bwd(z, z, st, st, g, b=1, s=t * T, t=t)
+    with pytest.raises(ValueError):
+        spr.bwd_dropout(z, z, st, st, g, b=1, s=t * T, t=t, rank=0, p_drop=0.1, seed=1)
+
+
 def test_python_layer_checks_cu_seqlens():
     spr.check_cu_seqlens([0, 3, 3, 8], 8)
     for bad, T in (([1, 8], 8), ([0, 5, 4, 8], 8), ([0, 7], 8), ([0], 0)):
