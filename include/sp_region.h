@@ -284,7 +284,9 @@ size_t sp_region_bwd_dropout_workspace_bytes(int64_t n_local_tokens, int64_t h);
  *                16-byte aligned.  Contents are scratch.
  *
  * Results are bitwise reproducible for a given (T, h); dx, dgamma and dbeta
- * are bitwise those of sp_region_bwd on the same inputs.
+ * are bitwise those of sp_region_bwd on the same inputs.  Without dbias,
+ * small shards take sp_region_bwd's one-launch path (its row blocks also
+ * write dpartial); a call that wants dbias always takes the partials path.
  */
 int sp_region_bwd_dropout(int64_t b, int64_t s, int64_t h, int32_t t,
                           const void* gamma, int32_t norm, int32_t dtype,

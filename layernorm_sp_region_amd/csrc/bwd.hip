@@ -565,17 +565,18 @@ __device__ __forceinline__ void col_block(const BwdParams& p, const ColOut& o, i
   }
 }
 
-// Blocks [0, G): rows (SHORT, at most R each, no column sums); blocks
-// [G, G + ceil(h / (kDirectLanes * V))): columns.  Nothing waits on another
-// block.
-template <class E, int VPT, int R, bool DRES, int MAXBS>
+// Blocks [0, G): rows (SHORT, at most R each, no column sums; with DROP they
+// also write dpartial); blocks [G, G + ceil(h / (kDirectLanes * V))):
+// columns, dgamma and dbeta only (dbias needs the row sums, so a call that
+// wants it takes the partials path).  Nothing waits on another block.
+template <class E, int VPT, int R, bool DRES, bool DROP, int MAXBS>
 __global__ __launch_bounds__(MAXBS) void sp_region_bwd_direct_kernel(const BwdParams p, const ColOut o) {
   if (static_cast<int>(blockIdx.x) >= p.G) {
     col_block<E, R>(p, o, static_cast<int>(blockIdx.x) - p.G);
     return;
   }
-  ColSums<VPT, E::kVec, false> cs;
-  rows_phase<E, VPT, R, true, DRES, false, int, false>(p, cs, 0);
+  ColSums<VPT, E::kVec, DROP> cs;
+  rows_phase<E, VPT, R, true, DRES, DROP, int, false>(p, cs, 0);
 }
 
 // Rows in flight for VPT vectors per thread: the packed rows take at most
@@ -644,17 +645,18 @@ hipError_t launch_rows(const BwdParams& p, const ColOut& o, int np, const Shape&
   constexpr int RR = ring_rows<VPT, DRES, DROP>();
   const dim3 grid(static_cast<unsigned>(p.G)), block(sh.threads);
   const int64_t rows_per_block = (p.T + p.G - 1) / p.G;
-  if constexpr (!DROP) {
-    // The direct path when the row blocks are short enough and every block
-    // of the launch can be resident at once (measured at s = h = 4096, t =
-    // 8, 512 local tokens: 128 row + 128 column blocks, 9.2 us against
-    // 15.9 us for the partials path).
+  {
+    // The direct path when the row blocks are short enough, every block of
+    // the launch can be resident at once, and no dbias is wanted (measured at
+    // s = h = 4096, t = 8, 512 local tokens: 128 row + 128 column blocks,
+    // 9.2 us against 15.9 us for the partials path).
     constexpr int RD = RS < 4 ? RS : 4;
     const int gcols = (p.h / E::kVec + kDirectLanes - 1) / kDirectLanes;
-    if (g_max_launches.load(std::memory_order_relaxed) == 1 && rows_per_block <= RD && p.G <= kDirectMaxBlocks &&
-        p.G + gcols <= device_cus(stream)) {
-      launch_kernel(sp_region_bwd_direct_kernel<E, VPT, RD, DRES, MAXBS>, dim3(static_cast<unsigned>(p.G + gcols)),
-                    block, stream, KernelRole::kOnly, p, o);
+    const bool no_dbias = !DROP || p.slot_dbias == 0;
+    if (no_dbias && g_max_launches.load(std::memory_order_relaxed) == 1 && rows_per_block <= RD &&
+        p.G <= kDirectMaxBlocks && p.G + gcols <= device_cus(stream)) {
+      launch_kernel(sp_region_bwd_direct_kernel<E, VPT, RD, DRES, DROP, MAXBS>,
+                    dim3(static_cast<unsigned>(p.G + gcols)), block, stream, KernelRole::kOnly, p, o);
       return hipGetLastError();
     }
   }

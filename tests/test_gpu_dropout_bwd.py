@@ -70,6 +70,53 @@ def test_workload_dropout_backward(cuda_device, name, rank):
     check(w, inp, rank, two)
 
 
+@pytest.mark.parametrize("name,rank", [("page_demo", 2), ("tiny", 1)])
+def test_dropout_backward_without_dbias(cuda_device, name, rank):
+    """Without dbias, small shards take the one-launch backward (row blocks
+    write dx and dpartial, column blocks sum dgamma/dbeta): dpartial and dx
+    against the oracle, dgamma/dbeta bit for bit those of sp_region_bwd and
+    of the two-launch path."""
+    import torch
+    w = W.BY_NAME[name]
+    log(f"[dropout-bwd no dbias] {name} rank={rank}")
+    inp = inputs_for(w)
+    t = lambda a: W.as_torch(a, cuda_device)
+    fo = spr.fwd(t(inp["partials"]), t(inp["gamma"]), t(inp["beta"]), bias=t(inp["bias"]),
+                 residual=t(inp["residual"]), b=inp["b"], s=inp["s"], t=w.t, rank=rank, eps=w.eps, p_drop=w.p_drop,
+                 seed=inp["seed"], norm=w.norm, cu_seqlens=inp["cu_seqlens"])
+    dy, gamma = t(inp["dy"]), t(inp["gamma"])
+    kw = dict(b=inp["b"], s=inp["s"], t=w.t, norm=w.norm)
+    dkw = dict(kw, rank=rank, p_drop=w.p_drop, seed=inp["seed"], cu_seqlens=inp["cu_seqlens"], want_dbias=False)
+    one = spr.bwd(dy, fo.z, fo.mean, fo.rstd, gamma, **kw)
+    outs = {}
+    try:
+        for n in (1, 2):
+            spr.set_bwd_launches(n)
+            outs[n] = spr.bwd_dropout(dy, fo.z, fo.mean, fo.rstd, gamma, **dkw)
+    finally:
+        spr.set_bwd_launches(1)
+    torch.cuda.synchronize()
+    d = outs[1]
+    assert d.dbias is None
+    bits = lambda x: x.view(torch.int32 if x.dtype == torch.float32 else torch.int16).cpu()
+    for k in ("dx", "dgamma", "dbeta"):
+        assert torch.equal(bits(getattr(one, k)), bits(getattr(d, k))), f"{k} differs from sp_region_bwd"
+    for k in ("dx", "dpartial", "dgamma", "dbeta"):
+        assert torch.equal(bits(getattr(outs[2], k)), bits(getattr(d, k))), f"{k}: one launch against two"
+    o = ref.region_forward(inp["partials"], t=w.t, rank=rank, dtype=w.dtype, norm=w.norm, eps=w.eps,
+                           p_drop=w.p_drop, seed=inp["seed"], gamma=inp["gamma"], beta=inp["beta"],
+                           bias=inp["bias"], residual=inp["residual"], cu_seqlens=inp["cu_seqlens"])
+    ob = ref.region_backward(inp["dy"], o["z"], inp["gamma"], dtype=w.dtype, norm=w.norm, eps=w.eps)
+    od = ref.dropout_backward(ob["dx"], t=w.t, rank=rank, p_drop=w.p_drop, seed=inp["seed"],
+                              cu_seqlens=inp["cu_seqlens"])
+    got = to_np_f64(d.dpartial)
+    assert np.all(got[~od["keep"]] == 0.0), "dpartial nonzero where the forward dropped"
+    assert_out_close(got, od["dpartial"], w.dtype, "dpartial", 4e-5)
+    assert_out_close(to_np_f64(d.dx), ob["dx"], w.dtype, "dx", 3e-5)
+    err = np.abs(to_np_f64(d.dgamma) - ob["dgamma"])
+    assert np.all(err <= 1e-4 * ob["A"]), "dgamma"
+
+
 EDGE = [
     # ragged shard with dropout on: the token index comes from cu_seqlens (scalar loads)
     (W.custom("ragged_drop", h=1024, t=4, lengths=(40, 0, 96, 8, 200), norm="layernorm", p_drop=0.3), 2, True),
