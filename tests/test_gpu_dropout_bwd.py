@@ -70,22 +70,37 @@ def test_workload_dropout_backward(cuda_device, name, rank):
     check(w, inp, rank, two)
 
 
-@pytest.mark.parametrize("name,rank", [("page_demo", 2), ("tiny", 1)])
-def test_dropout_backward_without_dbias(cuda_device, name, rank):
+NO_DBIAS = [("page_demo", 2, False), ("tiny", 1, False),
+            # ragged shard: the token index of each row from cu_seqlens (scalar loads)
+            (W.custom("ragged_drop_small", h=1024, t=4, lengths=(40, 0, 96, 8, 200), norm="layernorm",
+                      p_drop=0.3), 3, False),
+            # odd t, b = 2, 65 vectors per row (a ragged last column block), extra gradient on z
+            (W.custom("odd_t3_h520_dres", h=520, t=3, s=3 * 37, b=2, p_drop=0.25), 2, True),
+            # float32 RMSNorm (dgamma only)
+            (W.custom("f32_rms_h768", h=768, t=2, s=2 * 50, dtype="f32", norm="rmsnorm", p_drop=0.5), 1, False)]
+
+
+@pytest.mark.parametrize("case,rank,with_dres", NO_DBIAS,
+                         ids=[c if isinstance(c, str) else c.name for c, _, _ in NO_DBIAS])
+def test_dropout_backward_without_dbias(cuda_device, case, rank, with_dres):
     """Without dbias, small shards take the one-launch backward (row blocks
     write dx and dpartial, column blocks sum dgamma/dbeta): dpartial and dx
     against the oracle, dgamma/dbeta bit for bit those of sp_region_bwd and
     of the two-launch path."""
     import torch
-    w = W.BY_NAME[name]
-    log(f"[dropout-bwd no dbias] {name} rank={rank}")
-    inp = inputs_for(w)
+    w = W.BY_NAME[case] if isinstance(case, str) else case
+    name = w.name
+    log(f"[dropout-bwd no dbias] {name} rank={rank} dres={with_dres}")
+    inp = inputs_for(w) if isinstance(case, str) else W.make_inputs(w)
+    dres = None
+    if with_dres:
+        dres = W.make_inputs(W.custom(w.name + "_g", h=w.h, t=w.t, s=w.t * inp["T"], dtype=w.dtype, seed=98))["dy"]
     t = lambda a: W.as_torch(a, cuda_device)
     fo = spr.fwd(t(inp["partials"]), t(inp["gamma"]), t(inp["beta"]), bias=t(inp["bias"]),
                  residual=t(inp["residual"]), b=inp["b"], s=inp["s"], t=w.t, rank=rank, eps=w.eps, p_drop=w.p_drop,
                  seed=inp["seed"], norm=w.norm, cu_seqlens=inp["cu_seqlens"])
     dy, gamma = t(inp["dy"]), t(inp["gamma"])
-    kw = dict(b=inp["b"], s=inp["s"], t=w.t, norm=w.norm)
+    kw = dict(b=inp["b"], s=inp["s"], t=w.t, norm=w.norm, dres_in=t(dres))
     dkw = dict(kw, rank=rank, p_drop=w.p_drop, seed=inp["seed"], cu_seqlens=inp["cu_seqlens"], want_dbias=False)
     one = spr.bwd(dy, fo.z, fo.mean, fo.rstd, gamma, **kw)
     outs = {}
@@ -100,13 +115,18 @@ def test_dropout_backward_without_dbias(cuda_device, name, rank):
     assert d.dbias is None
     bits = lambda x: x.view(torch.int32 if x.dtype == torch.float32 else torch.int16).cpu()
     for k in ("dx", "dgamma", "dbeta"):
-        assert torch.equal(bits(getattr(one, k)), bits(getattr(d, k))), f"{k} differs from sp_region_bwd"
+        a, b = getattr(one, k), getattr(d, k)
+        assert (a is None) == (b is None), k
+        if a is not None:
+            assert torch.equal(bits(a), bits(b)), f"{k} differs from sp_region_bwd"
     for k in ("dx", "dpartial", "dgamma", "dbeta"):
-        assert torch.equal(bits(getattr(outs[2], k)), bits(getattr(d, k))), f"{k}: one launch against two"
+        a, b = getattr(outs[2], k), getattr(d, k)
+        if a is not None:
+            assert torch.equal(bits(a), bits(b)), f"{k}: one launch against two"
     o = ref.region_forward(inp["partials"], t=w.t, rank=rank, dtype=w.dtype, norm=w.norm, eps=w.eps,
                            p_drop=w.p_drop, seed=inp["seed"], gamma=inp["gamma"], beta=inp["beta"],
                            bias=inp["bias"], residual=inp["residual"], cu_seqlens=inp["cu_seqlens"])
-    ob = ref.region_backward(inp["dy"], o["z"], inp["gamma"], dtype=w.dtype, norm=w.norm, eps=w.eps)
+    ob = ref.region_backward(inp["dy"], o["z"], inp["gamma"], dtype=w.dtype, norm=w.norm, eps=w.eps, dres_in=dres)
     od = ref.dropout_backward(ob["dx"], t=w.t, rank=rank, p_drop=w.p_drop, seed=inp["seed"],
                               cu_seqlens=inp["cu_seqlens"])
     got = to_np_f64(d.dpartial)
